@@ -1,0 +1,26 @@
+"""CPU float64 oracle for DualKV shared-prompt attention.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the CPU
+baseline leg of the benchmark may import this package. The product path (the
+HIP library and its Python binding) never imports it, and this package never
+imports the product path: the two share no code. Inputs are plain numpy arrays.
+
+Two independent formulations of the same definition live here:
+
+* ``replicated`` -- the literal one. The shared prompt is copied into N ordinary
+  causal sequences [prompt; response_n], each is run through textbook softmax
+  attention and its textbook backward, and the results are gathered back into
+  the packed layout, summing the N copies' prompt gradients. This is what the
+  DualKV pages (abstract on p2; "Approach" on p1) say the fused kernels are
+  exactly equivalent to.
+* ``sampled`` -- the packed definition written out per query row and per key:
+  row t attends A(t) = {0..t} for a prompt row and {0..P-1} u {o_n..t} for a row
+  of response n. It evaluates selected rows/keys at full workload sizes, where
+  the literal replication is too slow to run whole.
+
+Every function in both modules has a pin in tests/test_oracle.py against
+something other than itself (library attention + autograd, closed forms,
+finite differences, invariants).
+"""
+from .replicated import oracle_fwd_bwd, causal_attention_fwd, causal_attention_bwd  # noqa: F401
+from .sampled import attended_keys, rows_fwd_bwd, keys_dkdv  # noqa: F401
