@@ -1,0 +1,9 @@
+"""MI355X (gfx950) shared-prompt attention: packed prompt + N responses.
+
+The forward and backward passes are HIP kernels in libdualkv.so behind the C
+ABI of include/dualkv.h; this package is the thin Python binding over it
+(`fwd`, `bwd`, `DualKVAttention`), plus seeded workload inputs and work/FLOP
+accounting used by the tests and the benchmark.
+"""
+from .binding import (DualKVAttention, DualKVError, Packing, bwd, bwd_workspace_bytes,  # noqa: F401
+                      fwd, fwd_workspace_bytes, load)

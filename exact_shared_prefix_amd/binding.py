@@ -1,0 +1,196 @@
+"""Thin ctypes binding over libdualkv.so (include/dualkv.h).
+
+Argument marshalling only: torch provides device memory and the current
+stream; every step of the computation runs in the library's HIP kernels.
+There is no fallback: if the library is missing or cannot be loaded, every
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdualkv.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+EXPORTS = ("dualkv_fwd_workspace_bytes", "dualkv_bwd_workspace_bytes", "dualkv_fwd",
+           "dualkv_bwd", "dualkv_status_string")
+
+_lib = None
+
+
+class DualKVError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the library (build it first if it was never built here)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(path)
+    c_int, c_size, c_float, vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.dualkv_fwd_workspace_bytes.restype = c_size
+    lib.dualkv_fwd_workspace_bytes.argtypes = [c_int, c_int, c_int, i32p, c_int, c_int, c_int]
+    lib.dualkv_bwd_workspace_bytes.restype = c_size
+    lib.dualkv_bwd_workspace_bytes.argtypes = [c_int, c_int, c_int, i32p, c_int, c_int, c_int, c_int]
+    lib.dualkv_fwd.restype = c_int
+    lib.dualkv_fwd.argtypes = [vp, vp, vp, vp, vp, c_int, c_int, c_int, i32p, c_int, c_int, c_int,
+                               c_float, vp, c_size, vp]
+    lib.dualkv_bwd.restype = c_int
+    lib.dualkv_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, c_int, c_int, c_int, i32p,
+                               c_int, c_int, c_int, c_float, c_int, vp, c_size, vp]
+    lib.dualkv_status_string.restype = ctypes.c_char_p
+    lib.dualkv_status_string.argtypes = [c_int]
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().dualkv_status_string(status).decode()
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        raise DualKVError(status, status_string(status))
+
+
+class Packing:
+    """P and the response lengths, as the ABI wants them (R or offsets)."""
+
+    def __init__(self, P: int, lengths: Optional[Sequence[int]] = None, R: Optional[int] = None,
+                 N: Optional[int] = None):
+        self.P = int(P)
+        if lengths is None:
+            if R is None or N is None:
+                raise ValueError("give lengths, or both R and N")
+            lengths = [int(R)] * int(N)
+        self.lengths = [int(x) for x in lengths]
+        self.N = len(self.lengths)
+        self.uniform = self.N > 0 and all(x == self.lengths[0] for x in self.lengths)
+        self.R = self.lengths[0] if self.uniform else 0
+        offs = [self.P]
+        for x in self.lengths:
+            offs.append(offs[-1] + x)
+        self.T = offs[-1]
+        self._offsets = (ctypes.c_int32 * (self.N + 1))(*offs)
+
+    def offsets_ptr(self):
+        if self.uniform:
+            return None
+        return ctypes.cast(self._offsets, ctypes.POINTER(ctypes.c_int32))
+
+
+def _stream_ptr(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check_tensor(name, t, shape, dtype, device):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+
+
+def fwd_workspace_bytes(pk: Packing, Hq: int, Hkv: int, d: int) -> int:
+    n = load().dualkv_fwd_workspace_bytes(pk.P, pk.R, pk.N, pk.offsets_ptr(), Hq, Hkv, d)
+    if n == 0:
+        raise DualKVError(ERR_INVALID_ARG, "invalid problem shape")
+    return n
+
+
+def bwd_workspace_bytes(pk: Packing, Hq: int, Hkv: int, d: int, deterministic: bool = False) -> int:
+    n = load().dualkv_bwd_workspace_bytes(pk.P, pk.R, pk.N, pk.offsets_ptr(), Hq, Hkv, d,
+                                          int(deterministic))
+    if n == 0:
+        raise DualKVError(ERR_UNSUPPORTED if deterministic else ERR_INVALID_ARG,
+                          "invalid problem shape or unsupported mode")
+    return n
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pk: Packing,
+        scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+        lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+        stream=None):
+    """dualkv_fwd. q [T,Hq,d], k/v [T,Hkv,d] bf16 on the GPU -> (o, lse)."""
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    _check_tensor("q", q, (pk.T, Hq, d), torch.bfloat16, dev)
+    _check_tensor("k", k, (pk.T, Hkv, d), torch.bfloat16, dev)
+    _check_tensor("v", v, (pk.T, Hkv, d), torch.bfloat16, dev)
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((Hq, pk.T), dtype=torch.float32, device=dev)
+    _check_tensor("o", out, (pk.T, Hq, d), torch.bfloat16, dev)
+    _check_tensor("lse", lse, (Hq, pk.T), torch.float32, dev)
+    nws = fwd_workspace_bytes(pk, Hq, Hkv, d)
+    if workspace is None or workspace.numel() < nws:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+    _check(load().dualkv_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), pk.P, pk.R, pk.N,
+                             pk.offsets_ptr(), Hq, Hkv, d, float(scale), _ptr(workspace),
+                             workspace.numel(), _stream_ptr(stream)))
+    return out, lse
+
+
+def bwd(q, k, v, o, lse, do, pk: Packing, scale: Optional[float] = None,
+        dq=None, dk=None, dv=None, workspace=None, deterministic: bool = False, stream=None):
+    """dualkv_bwd -> (dq, dk, dv), bf16, same layouts as q, k, v."""
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    for name, t, hh in (("q", q, Hq), ("o", o, Hq), ("do", do, Hq), ("k", k, Hkv), ("v", v, Hkv)):
+        _check_tensor(name, t, (pk.T, hh, d), torch.bfloat16, dev)
+    _check_tensor("lse", lse, (Hq, pk.T), torch.float32, dev)
+    if scale is None:
+        scale = d ** -0.5
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    nws = bwd_workspace_bytes(pk, Hq, Hkv, d, deterministic)
+    if workspace is None or workspace.numel() < nws:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+    _check(load().dualkv_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
+                             _ptr(dk), _ptr(dv), pk.P, pk.R, pk.N, pk.offsets_ptr(), Hq, Hkv, d,
+                             float(scale), int(deterministic), _ptr(workspace), workspace.numel(),
+                             _stream_ptr(stream)))
+    return dq, dk, dv
+
+
+class DualKVAttention(torch.autograd.Function):
+    """Autograd wrapper: forward and backward both run in libdualkv."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, pk: Packing, scale=None):
+        o, lse = fwd(q, k, v, pk, scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.pk, ctx.scale = pk, scale
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = bwd(q, k, v, o, lse, do.contiguous(), ctx.pk, ctx.scale)
+        return dq, dk, dv, None, None

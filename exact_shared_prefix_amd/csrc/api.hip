@@ -1,0 +1,212 @@
+// C ABI: argument checks, packed-layout descriptors, work lists, launches.
+//
+// The packed layout is the DualKV one (p2 abstract: P + NR tokens per
+// micro-batch; p1 "Approach": a shared-context KV region and per-sequence
+// response KV regions). Work lists are built on the host and copied into the
+// caller's workspace on the caller's stream; nothing is allocated here.
+#include <algorithm>
+#include <cmath>
+#include <vector>
+
+#include "../../include/dualkv.h"
+#include "common.h"
+
+namespace dkv {
+hipError_t launch_fwd(const Problem& pb, const void* q, const void* k, const void* v, void* o,
+                      float* lse, const FwdItem* items_dev, int n_items, hipStream_t stream);
+hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const void* v,
+                      const void* o, const float* lse, const void* dO, void* dQ, void* dK,
+                      void* dV, const BwdItem* items_dev, int n_items, float* delta,
+                      float* dq_acc, float* dk_acc, float* dv_acc, hipStream_t stream);
+}  // namespace dkv
+
+using namespace dkv;
+
+namespace {
+
+constexpr int kFwdRows = 128;   // query rows per forward workgroup
+constexpr int kBwdKeys = 128;   // keys per backward workgroup
+constexpr int kBwdChunk = 1024; // query rows per backward work item (grid of row chunks)
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Shape checks shared by every entry point. Fills pb on success.
+dualkv_status check_shape(int P, int R, int N, const int32_t* offsets, int Hq, int Hkv, int d,
+                          Problem& pb) {
+  if (P < 0 || N < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return DUALKV_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return DUALKV_ERR_UNSUPPORTED;
+  long long T;
+  if (offsets) {
+    if (offsets[0] != P) return DUALKV_ERR_INVALID_ARG;
+    for (int n = 0; n < N; ++n)
+      if (offsets[n + 1] < offsets[n]) return DUALKV_ERR_INVALID_ARG;
+    T = offsets[N];
+  } else {
+    if (R < 0) return DUALKV_ERR_INVALID_ARG;
+    T = (long long)P + (long long)N * R;
+  }
+  if (T >= (1LL << 31)) return DUALKV_ERR_INVALID_ARG;
+  if (T * (long long)std::max(Hq, Hkv) * d >= (1LL << 31)) return DUALKV_ERR_INVALID_ARG;
+  pb.P = P;
+  pb.N = N;
+  pb.R = offsets ? 0 : R;
+  pb.offsets = offsets;
+  pb.T = (int)T;
+  pb.Hq = Hq;
+  pb.Hkv = Hkv;
+  pb.G = Hq / Hkv;
+  pb.d = d;
+  return DUALKV_OK;
+}
+
+bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Forward work list: 128-row query tiles that never straddle a segment,
+// longest (most keys) first so the tail of the grid is short.
+std::vector<FwdItem> fwd_items(const Problem& pb) {
+  std::vector<FwdItem> items;
+  for (int r = 0; r < pb.P; r += kFwdRows) {
+    const int r1 = std::min(pb.P, r + kFwdRows);
+    items.push_back({r, r1, r1, r1});
+  }
+  for (int n = 0; n < pb.N; ++n) {
+    const int a = pb.seg_start(n), b = pb.seg_start(n + 1);
+    for (int r = a; r < b; r += kFwdRows) items.push_back({r, std::min(b, r + kFwdRows), pb.P, a});
+  }
+  std::stable_sort(items.begin(), items.end(), [](const FwdItem& x, const FwdItem& y) {
+    return (x.a_end + x.r1 - x.b_start) > (y.a_end + y.r1 - y.b_start);
+  });
+  return items;
+}
+
+// Backward work list: 128-key tiles, each paired with the rows that attend it
+// (all later rows for a prompt tile, the later rows of its own response for a
+// response tile), cut on a fixed grid of kBwdChunk-row chunks. Items are
+// ordered chunk-major so workgroups running together share query rows.
+std::vector<BwdItem> bwd_items(const Problem& pb) {
+  struct Tile { int kb, ke, rend; };
+  std::vector<Tile> tiles;
+  for (int kb = 0; kb < pb.P; kb += kBwdKeys) tiles.push_back({kb, std::min(pb.P, kb + kBwdKeys), pb.T});
+  for (int n = 0; n < pb.N; ++n) {
+    const int a = pb.seg_start(n), b = pb.seg_start(n + 1);
+    for (int kb = a; kb < b; kb += kBwdKeys) tiles.push_back({kb, std::min(b, kb + kBwdKeys), b});
+  }
+  std::vector<BwdItem> items;
+  const int nchunks = (pb.T + kBwdChunk - 1) / kBwdChunk;
+  for (int cidx = 0; cidx < nchunks; ++cidx) {
+    const int c0 = cidx * kBwdChunk, c1 = std::min(pb.T, c0 + kBwdChunk);
+    for (const Tile& tl : tiles) {
+      const int r0 = std::max(c0, tl.kb), r1 = std::min(c1, tl.rend);
+      if (r0 < r1) items.push_back({tl.kb, tl.ke, r0, r1});
+    }
+  }
+  return items;
+}
+
+struct BwdLayout {
+  size_t items, delta, dq, dk, dv, total;
+};
+
+BwdLayout bwd_layout(const Problem& pb, size_t n_items) {
+  BwdLayout L;
+  size_t off = 0;
+  L.items = off; off = align_up(off + n_items * sizeof(BwdItem));
+  L.delta = off; off = align_up(off + (size_t)pb.Hq * pb.T * sizeof(float));
+  L.dq = off;    off = align_up(off + (size_t)pb.T * pb.Hq * pb.d * sizeof(float));
+  L.dk = off;    off = align_up(off + (size_t)pb.T * pb.Hkv * pb.d * sizeof(float));
+  L.dv = off;    off = align_up(off + (size_t)pb.T * pb.Hkv * pb.d * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dualkv_fwd_workspace_bytes(int P, int R, int N, const int32_t* offsets, int Hq, int Hkv,
+                                  int d) {
+  Problem pb;
+  if (check_shape(P, R, N, offsets, Hq, Hkv, d, pb) != DUALKV_OK) return 0;
+  return align_up(std::max<size_t>(1, fwd_items(pb).size()) * sizeof(FwdItem));
+}
+
+size_t dualkv_bwd_workspace_bytes(int P, int R, int N, const int32_t* offsets, int Hq, int Hkv,
+                                  int d, int deterministic) {
+  Problem pb;
+  if (deterministic) return 0;
+  if (check_shape(P, R, N, offsets, Hq, Hkv, d, pb) != DUALKV_OK) return 0;
+  return bwd_layout(pb, std::max<size_t>(1, bwd_items(pb).size())).total;
+}
+
+dualkv_status dualkv_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int P,
+                         int R, int N, const int32_t* offsets, int Hq, int Hkv, int d,
+                         float softmax_scale, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  Problem pb;
+  dualkv_status st = check_shape(P, R, N, offsets, Hq, Hkv, d, pb);
+  if (st != DUALKV_OK) return st;
+  if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return DUALKV_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return DUALKV_ERR_INVALID_ARG;
+  pb.scale = softmax_scale;
+  const std::vector<FwdItem> items = fwd_items(pb);
+  const size_t need = align_up(std::max<size_t>(1, items.size()) * sizeof(FwdItem));
+  if (!workspace || workspace_bytes < need) return DUALKV_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return DUALKV_ERR_INVALID_ARG;
+  if (items.empty()) return DUALKV_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(workspace, items.data(), items.size() * sizeof(FwdItem), hipMemcpyHostToDevice,
+                     s) != hipSuccess)
+    return DUALKV_ERR_HIP;
+  if (launch_fwd(pb, q, k, v, o, lse, static_cast<const FwdItem*>(workspace), (int)items.size(),
+                 s) != hipSuccess)
+    return DUALKV_ERR_HIP;
+  return DUALKV_OK;
+}
+
+dualkv_status dualkv_bwd(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dO, void* dQ, void* dK, void* dV, int P,
+                         int R, int N, const int32_t* offsets, int Hq, int Hkv, int d,
+                         float softmax_scale, int deterministic, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  Problem pb;
+  dualkv_status st = check_shape(P, R, N, offsets, Hq, Hkv, d, pb);
+  if (st != DUALKV_OK) return st;
+  if (deterministic) return DUALKV_ERR_UNSUPPORTED;
+  if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return DUALKV_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(dO) || !aligned16(dQ) || !aligned16(dK) || !aligned16(dV))
+    return DUALKV_ERR_INVALID_ARG;
+  pb.scale = softmax_scale;
+  const std::vector<BwdItem> items = bwd_items(pb);
+  const BwdLayout L = bwd_layout(pb, std::max<size_t>(1, items.size()));
+  if (!workspace || workspace_bytes < L.total) return DUALKV_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return DUALKV_ERR_INVALID_ARG;
+  if (pb.T == 0) return DUALKV_OK;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!items.empty() &&
+      hipMemcpyAsync(ws + L.items, items.data(), items.size() * sizeof(BwdItem),
+                     hipMemcpyHostToDevice, s) != hipSuccess)
+    return DUALKV_ERR_HIP;
+  if (launch_bwd(pb, q, k, v, o, lse, dO, dQ, dK, dV, reinterpret_cast<const BwdItem*>(ws + L.items),
+                 (int)items.size(), reinterpret_cast<float*>(ws + L.delta),
+                 reinterpret_cast<float*>(ws + L.dq), reinterpret_cast<float*>(ws + L.dk),
+                 reinterpret_cast<float*>(ws + L.dv), s) != hipSuccess)
+    return DUALKV_ERR_HIP;
+  return DUALKV_OK;
+}
+
+const char* dualkv_status_string(dualkv_status s) {
+  switch (s) {
+    case DUALKV_OK: return "ok";
+    case DUALKV_ERR_INVALID_ARG: return "invalid argument";
+    case DUALKV_ERR_UNSUPPORTED: return "unsupported head_dim or mode";
+    case DUALKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case DUALKV_ERR_HIP: return "HIP runtime or kernel launch error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,354 @@
+// Backward kernels for shared-prompt attention.
+//
+// DualKV pages (p1 "Approach"): the backward walks the same two disjoint KV
+// regions as the forward and accumulates the shared prompt's key/value
+// gradients over all N sequences with fp32 atomics. Here:
+//  1. pre_kernel:  D_t = sum_d dO_t * O_t (fp32), and zero-fill of the fp32
+//                  accumulators for dQ, dK, dV.
+//  2. main_kernel: KV-stationary. A workgroup owns 128 keys of one KV head
+//                  (4 waves x 32 keys, K and V fragments in registers) and
+//                  walks a chunk of query rows in blocks of 32 rows, for each
+//                  of the G query heads of the group:
+//                    S = Q K^T, P = exp2(S c - LSE_2), dP = dO V^T,
+//                    dS = P (dP - D), dV += P^T dO, dK += dS^T Q,
+//                    dQ += dS K (fp32 atomics into the dQ accumulator).
+//                  A prompt tile's rows are every later row of the packed
+//                  batch, split into row chunks so the work spreads over the
+//                  chip; partial dK/dV of every chunk are added with fp32
+//                  atomics, which is where the N sequences' prompt gradients
+//                  meet.
+//  3. convert_kernel: fp32 accumulators -> bf16 (dQ, dK scaled by the softmax
+//                  scale here once).
+// MFMA orientation: S is computed with queries as rows, so a lane owns one key
+// column and the S/dS accumulators serve directly as the A operand of
+// dV = P^T dO and dK = dS^T Q. dS takes one trip through LDS for dQ = dS K.
+#include "common.h"
+
+namespace dkv {
+
+// ------------------------------------------------------------------ pre --
+// One 16-lane group per (row, head): 16 lanes x 8 elements = 128 (d=64: 8 lanes).
+template <int D>
+__global__ __launch_bounds__(256) void pre_kernel(const u16* __restrict__ o,
+                                                  const u16* __restrict__ dO,
+                                                  float* __restrict__ delta, int T, int Hq) {
+  constexpr int LPR = D / 8;  // lanes per (row, head)
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long rh = gid / LPR;   // row * Hq + head
+  const int sub = (int)(gid % LPR);
+  float acc = 0.f;
+  const bool valid = rh < (long long)T * Hq;
+  if (valid) {
+    const uint4 a = *reinterpret_cast<const uint4*>(o + rh * D + sub * 8);
+    const uint4 b = *reinterpret_cast<const uint4*>(dO + rh * D + sub * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = __uint_as_float(u16_of(a, e) << 16);
+      float y = __uint_as_float(u16_of(b, e) << 16);
+      acc = fmaf(x, y, acc);
+    }
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (valid && sub == 0) {
+    const int t = (int)(rh / Hq), h = (int)(rh % Hq);
+    delta[(size_t)h * T + t] = acc;
+  }
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(float4* __restrict__ p, size_t n4) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256)
+    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// ------------------------------------------------------------------ main --
+template <int D>
+__global__ __launch_bounds__(256, 1) void main_kernel(
+    const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
+    const u16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
+    float* __restrict__ dq_acc, float* __restrict__ dk_acc, float* __restrict__ dv_acc,
+    const BwdItem* __restrict__ items, HeadMap hm, int T, int Hq, int Hkv, float c) {
+  constexpr int BKW = 128;       // keys per workgroup
+  constexpr int BQ = 32;         // query rows per step
+  constexpr int NDC = D / 8;     // 8-element chunks per row
+  constexpr int RS = D + 8;      // row-layout stride (Qs, dOs)
+  constexpr int TS = BQ + 4;     // transposed stride (Qt, dOt)
+  constexpr int KTS = BKW + 8;   // K^T stride
+  constexpr int SS = BKW + 8;    // dS stride
+  __shared__ __attribute__((aligned(16))) u16 Qs[BQ * RS];
+  __shared__ __attribute__((aligned(16))) u16 dOs[BQ * RS];
+  __shared__ __attribute__((aligned(16))) u16 Qt[D * TS];
+  __shared__ __attribute__((aligned(16))) u16 dOt[D * TS];
+  __shared__ __attribute__((aligned(16))) u16 Kt[D * KTS];
+  __shared__ __attribute__((aligned(16))) u16 dSs[BQ * SS];
+  __shared__ __attribute__((aligned(16))) float lse2s[BQ];
+  __shared__ __attribute__((aligned(16))) float dels[BQ];
+
+  int item_id, g;
+  if (!headmap_decode(hm, blockIdx.x, item_id, g)) return;
+  const BwdItem it = items[item_id];
+  const int G = Hq / Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int hl = lane >> 5, l32 = lane & 31;
+  const size_t qrow = (size_t)Hq * D, krow = (size_t)Hkv * D;
+  const int kw = it.kb + 32 * w;          // first key of this wave
+  const int key = kw + l32;               // this lane's key (S/dP column)
+  const bool wave_keys = kw < it.ke;
+
+  // K and V fragments: B operands of S = Q K^T and dP = dO V^T
+  // (lane -> key column, 8 consecutive d).
+  bf16x8 kf[D / 16], vf[D / 16];
+  {
+    const bool ok = key < it.ke;
+    const u16* kp = k + (size_t)key * krow + (size_t)g * D + 8 * hl;
+    const u16* vp = v + (size_t)key * krow + (size_t)g * D + 8 * hl;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      Frag a, b;
+      a.u = ok ? *reinterpret_cast<const uint4*>(kp + 16 * kk) : make_uint4(0, 0, 0, 0);
+      b.u = ok ? *reinterpret_cast<const uint4*>(vp + 16 * kk) : make_uint4(0, 0, 0, 0);
+      kf[kk] = a.v;
+      vf[kk] = b.v;
+    }
+  }
+  // K^T of the whole 128-key tile in LDS (B operand of dQ = dS K).
+  {
+    constexpr int NBLK = (BKW / 4) * NDC;  // (4 keys x 8 d) blocks
+    for (int blk = tid; blk < NBLK; blk += 256) {
+      const int kg = blk % (BKW / 4), dc = blk / (BKW / 4);
+      uint4 r4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kk = it.kb + 4 * kg + j;
+        r4[j] = kk < it.ke ? *reinterpret_cast<const uint4*>(k + (size_t)kk * krow + (size_t)g * D + dc * 8)
+                           : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint2 w2;
+        w2.x = u16_of(r4[0], e) | (u16_of(r4[1], e) << 16);
+        w2.y = u16_of(r4[2], e) | (u16_of(r4[3], e) << 16);
+        *reinterpret_cast<uint2*>(Kt + (dc * 8 + e) * KTS + 4 * kg) = w2;
+      }
+    }
+  }
+
+  f32x16 dkacc[D / 32], dvacc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) { dkacc[i] = f32x16{}; dvacc[i] = f32x16{}; }
+
+  // Q / dO block staging: threads [0, 8*NDC) carry Q, [8*NDC, 16*NDC) carry dO;
+  // each holds 4 rows x 8 d.
+  const int st = tid % (8 * NDC);
+  const bool st_q = tid < 8 * NDC, st_do = tid >= 8 * NDC && tid < 16 * NDC;
+  const int st_rg = st % 8, st_dc = st / 8;
+  uint4 sreg[4];
+  float lreg = 0.f, dreg = 0.f;
+
+  const int nqb = (it.r1 - it.r0 + BQ - 1) / BQ;
+  const int nsteps = nqb * G;
+  auto load_step = [&](int s) {
+    const int qb = it.r0 + (s / G) * BQ, h = g * G + (s % G);
+    if (st_q || st_do) {
+      const u16* base = (st_q ? q : dO) + (size_t)h * D + st_dc * 8;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = qb + 4 * st_rg + j;
+        sreg[j] = row < it.r1 ? *reinterpret_cast<const uint4*>(base + (size_t)row * qrow)
+                              : make_uint4(0, 0, 0, 0);
+      }
+    }
+    if (tid < BQ) {
+      const int row = qb + tid;
+      const bool ok = row < it.r1;
+      lreg = ok ? lse[(size_t)h * T + row] * kLog2e : INFINITY;
+      dreg = ok ? delta[(size_t)h * T + row] : 0.f;
+    }
+  };
+  auto store_step = [&]() {
+    if (st_q || st_do) {
+      u16* rowl = st_q ? Qs : dOs;
+      u16* trl = st_q ? Qt : dOt;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<uint4*>(rowl + (4 * st_rg + j) * RS + st_dc * 8) = sreg[j];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint2 w2;
+        w2.x = u16_of(sreg[0], e) | (u16_of(sreg[1], e) << 16);
+        w2.y = u16_of(sreg[2], e) | (u16_of(sreg[3], e) << 16);
+        *reinterpret_cast<uint2*>(trl + (st_dc * 8 + e) * TS + 4 * st_rg) = w2;
+      }
+    }
+    if (tid < BQ) { lse2s[tid] = lreg; dels[tid] = dreg; }
+  };
+
+  if (nsteps > 0) load_step(0);
+  for (int s = 0; s < nsteps; ++s) {
+    const int qb = it.r0 + (s / G) * BQ, h = g * G + (s % G);
+    __syncthreads();   // previous step finished with Qs/dOs/Qt/dOt/dSs
+    store_step();
+    __syncthreads();
+    if (s + 1 < nsteps) load_step(s + 1);
+
+    const bool wave_work = wave_keys && kw <= qb + BQ - 1;
+    if (wave_work) {
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+      const u16* qp = Qs + l32 * RS + 8 * hl;
+      const u16* op = dOs + l32 * RS + 8 * hl;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        sacc = mfma32(lds_b128(qp + 16 * kk), kf[kk], sacc);
+        dpacc = mfma32(lds_b128(op + 16 * kk), vf[kk], dpacc);
+      }
+      // element r: query row qb + 8 (r/4) + 4 hl + r%4, key column `key`
+      const bool need_mask = (kw + 31 > qb) || (kw + 32 > it.ke);
+      float p[16], ds[16];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const float4 l4 = *reinterpret_cast<const float4*>(lse2s + 8 * g4 + 4 * hl);
+        const float4 d4 = *reinterpret_cast<const float4*>(dels + 8 * g4 + 4 * hl);
+        const float la[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float da[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g4 + e;
+          float x = fast_exp2(fmaf(sacc[r], c, -la[e]));
+          if (need_mask) {
+            const int row = qb + 8 * g4 + 4 * hl + e;
+            if (key > row || key >= it.ke) x = 0.f;
+          }
+          p[r] = x;
+          ds[r] = x * (dpacc[r] - da[e]);
+        }
+      }
+      const bf16x8 pf0 = pack_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+      const bf16x8 pf1 = pack_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
+      const bf16x8 sf0 = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+      const bf16x8 sf1 = pack_bf16x8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
+      // dV[key][d] += P^T dO, dK[key][d] += dS^T Q; k-slot (hl, e) is query
+      // 16 ks + 4 hl + e (e < 4) or 16 ks + 8 + 4 hl + (e - 4).
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const u16* ot = dOt + (32 * dt + l32) * TS + 4 * hl;
+        const u16* qt = Qt + (32 * dt + l32) * TS + 4 * hl;
+        dvacc[dt] = mfma32(pf0, lds_2xb64(ot, ot + 8), dvacc[dt]);
+        dvacc[dt] = mfma32(pf1, lds_2xb64(ot + 16, ot + 24), dvacc[dt]);
+        dkacc[dt] = mfma32(sf0, lds_2xb64(qt, qt + 8), dkacc[dt]);
+        dkacc[dt] = mfma32(sf1, lds_2xb64(qt + 16, qt + 24), dkacc[dt]);
+      }
+      // dS (bf16) into LDS as [query][key] for the dQ product
+      const Frag f0{sf0}, f1{sf1};
+      u16* sp = dSs + 32 * w + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t word = r < 8 ? (r < 2 ? f0.u.x : r < 4 ? f0.u.y : r < 6 ? f0.u.z : f0.u.w)
+                                    : (r < 10 ? f1.u.x : r < 12 ? f1.u.y : r < 14 ? f1.u.z : f1.u.w);
+        const u16 val = (r & 1) ? (u16)(word >> 16) : (u16)(word & 0xffffu);
+        sp[(8 * (r >> 2) + 4 * hl + (r & 3)) * SS] = val;
+      }
+    } else {
+      // keys of this wave are all after the block's rows: dS is zero
+      u16* sp = dSs + 32 * w + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sp[(8 * (r >> 2) + 4 * hl + (r & 3)) * SS] = 0;
+    }
+    __syncthreads();
+    // dQ[q][d] += dS[q][key] K[key][d]: wave w produces d columns [32 w, 32 w + 32).
+    if (32 * w < D && it.kb <= qb + BQ - 1) {
+      f32x16 acc = f32x16{};
+      const u16* ap = dSs + l32 * SS + 8 * hl;
+      const u16* bp = Kt + (32 * w + l32) * KTS + 8 * hl;
+#pragma unroll
+      for (int ks = 0; ks < BKW / 16; ++ks) acc = mfma32(lds_b128(ap + 16 * ks), lds_b128(bp + 16 * ks), acc);
+      float* dqp = dq_acc + (size_t)h * D + 32 * w + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = qb + 8 * (r >> 2) + 4 * hl + (r & 3);
+        if (row < it.r1) unsafeAtomicAdd(dqp + (size_t)row * qrow, acc[r]);
+      }
+    }
+  }
+
+  // partial dK / dV of this chunk: fp32 atomics (the cross-sequence prompt sum)
+  if (wave_keys) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kk = kw + 8 * (r >> 2) + 4 * hl + (r & 3);
+        if (kk < it.ke) {
+          const size_t off = (size_t)kk * krow + (size_t)g * D + 32 * dt + l32;
+          unsafeAtomicAdd(dk_acc + off, dkacc[dt][r]);
+          unsafeAtomicAdd(dv_acc + off, dvacc[dt][r]);
+        }
+      }
+  }
+}
+
+// --------------------------------------------------------------- convert --
+// dQ = bf16(scale * dQacc), dK = bf16(scale * dKacc), dV = bf16(dVacc).
+__global__ __launch_bounds__(256) void convert_kernel(const float4* __restrict__ src,
+                                                      uint2* __restrict__ dst, size_t n4,
+                                                      float mul) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+    const float4 x = src[i];
+    uint2 r;
+    r.x = pack_bf16x2(x.x * mul, x.y * mul);
+    r.y = pack_bf16x2(x.z * mul, x.w * mul);
+    dst[i] = r;
+  }
+}
+
+static int stream_grid(size_t n4) {
+  size_t b = (n4 + 255) / 256;
+  return (int)(b < 8192 ? (b ? b : 1) : 8192);
+}
+
+hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const void* v,
+                      const void* o, const float* lse, const void* dO, void* dQ, void* dK,
+                      void* dV, const BwdItem* items_dev, int n_items, float* delta,
+                      float* dq_acc, float* dk_acc, float* dv_acc, hipStream_t stream) {
+  const size_t nq = (size_t)pb.T * pb.Hq * pb.d, nk = (size_t)pb.T * pb.Hkv * pb.d;
+  // 1. D and zeroed accumulators
+  {
+    const long long lanes = (long long)pb.T * pb.Hq * (pb.d / 8);
+    dim3 grid((unsigned)((lanes + 255) / 256));
+    if (pb.d == 128)
+      hipLaunchKernelGGL(pre_kernel<128>, grid, dim3(256), 0, stream, (const u16*)o,
+                         (const u16*)dO, delta, pb.T, pb.Hq);
+    else
+      hipLaunchKernelGGL(pre_kernel<64>, grid, dim3(256), 0, stream, (const u16*)o,
+                         (const u16*)dO, delta, pb.T, pb.Hq);
+    hipLaunchKernelGGL(zero_kernel, dim3(stream_grid(nq / 4)), dim3(256), 0, stream,
+                       (float4*)dq_acc, nq / 4);
+    hipLaunchKernelGGL(zero_kernel, dim3(stream_grid(nk / 4)), dim3(256), 0, stream,
+                       (float4*)dk_acc, nk / 4);
+    hipLaunchKernelGGL(zero_kernel, dim3(stream_grid(nk / 4)), dim3(256), 0, stream,
+                       (float4*)dv_acc, nk / 4);
+  }
+  // 2. main
+  if (n_items > 0) {
+    HeadMap hm = make_headmap(n_items, pb.Hkv);
+    dim3 grid(headmap_grid(hm));
+    const float c = pb.scale * kLog2e;
+    if (pb.d == 128)
+      hipLaunchKernelGGL(main_kernel<128>, grid, dim3(256), 0, stream, (const u16*)q,
+                         (const u16*)k, (const u16*)v, (const u16*)dO, lse, delta, dq_acc,
+                         dk_acc, dv_acc, items_dev, hm, pb.T, pb.Hq, pb.Hkv, c);
+    else
+      hipLaunchKernelGGL(main_kernel<64>, grid, dim3(256), 0, stream, (const u16*)q,
+                         (const u16*)k, (const u16*)v, (const u16*)dO, lse, delta, dq_acc,
+                         dk_acc, dv_acc, items_dev, hm, pb.T, pb.Hq, pb.Hkv, c);
+  }
+  // 3. convert
+  hipLaunchKernelGGL(convert_kernel, dim3(stream_grid(nq / 4)), dim3(256), 0, stream,
+                     (const float4*)dq_acc, (uint2*)dQ, nq / 4, pb.scale);
+  hipLaunchKernelGGL(convert_kernel, dim3(stream_grid(nk / 4)), dim3(256), 0, stream,
+                     (const float4*)dk_acc, (uint2*)dK, nk / 4, pb.scale);
+  hipLaunchKernelGGL(convert_kernel, dim3(stream_grid(nk / 4)), dim3(256), 0, stream,
+                     (const float4*)dv_acc, (uint2*)dV, nk / 4, 1.0f);
+  return hipGetLastError();
+}
+
+}  // namespace dkv

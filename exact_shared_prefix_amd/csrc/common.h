@@ -1,0 +1,133 @@
+// Internal definitions shared by the forward/backward kernels and the C ABI.
+// gfx950 (CDNA4) only: wave64, bf16 MFMA 32x32x16, LDS tiles.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace dkv {
+
+typedef unsigned short u16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- problem --
+// Host-side description of one packed micro-batch.
+struct Problem {
+  int P = 0;          // prompt tokens
+  int N = 0;          // responses
+  int T = 0;          // packed tokens
+  int Hq = 0, Hkv = 0, G = 0, d = 0;
+  float scale = 0.f;  // softmax scale
+  const int32_t* offsets = nullptr;  // host, N+1 entries (o_0 = P ... o_N = T)
+  int R = 0;          // uniform response length when offsets == nullptr
+  int seg_start(int n) const { return offsets ? offsets[n] : P + n * R; }
+};
+
+// Forward work item: query rows [r0, r1) of one segment; KV region A is
+// [0, a_end) (the prompt, or the prompt rows up to r1 for a prompt tile) and
+// region B is [b_start, r1) (the own response; empty for a prompt tile).
+struct FwdItem { int r0, r1, a_end, b_start; };
+
+// Backward work item: keys [kb, ke) of one KV tile, query rows [r0, r1).
+// Every row in [r0, r1) with row >= key attends the key (prompt keys are seen
+// by all later rows, response keys only by their own response's later rows,
+// and the scheduler never pairs a response tile with foreign rows).
+struct BwdItem { int kb, ke, r0, r1; };
+
+// Launch-time block -> (item, head) decomposition that keeps each head group
+// on one XCD (workgroups are dealt to the 8 XCDs round-robin by block id).
+struct HeadMap { int n_items, H, mode; };
+
+__host__ __device__ inline int headmap_grid(const HeadMap& m) {
+  if (m.mode == 1) return m.n_items * m.H;
+  if (m.mode == 2) { int rep = 8 / m.H; return ((m.n_items + rep - 1) / rep) * 8; }
+  return m.n_items * m.H;
+}
+
+__host__ __device__ inline HeadMap make_headmap(int n_items, int H) {
+  HeadMap m{n_items, H, 0};
+  if (H % 8 == 0) m.mode = 1;
+  else if (8 % H == 0) m.mode = 2;
+  return m;
+}
+
+// returns false for padding blocks
+__device__ inline bool headmap_decode(const HeadMap& m, int b, int& item, int& head) {
+  if (m.mode == 1) {
+    int hp = m.H >> 3, x = b & 7, s = b >> 3;
+    head = x * hp + s % hp;
+    item = s / hp;
+  } else if (m.mode == 2) {
+    int rep = 8 / m.H, x = b & 7, s = b >> 3;
+    head = x % m.H;
+    item = s * rep + x / m.H;
+  } else {
+    item = b / m.H;
+    head = b % m.H;
+  }
+  return item < m.n_items;
+}
+
+// ----------------------------------------------------------------- device --
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+union Frag {
+  bf16x8 v;
+  uint4 u;
+  uint2 h[2];
+};
+
+__device__ __forceinline__ bf16x8 lds_b128(const u16* p) {
+  Frag f;
+  f.u = *reinterpret_cast<const uint4*>(p);
+  return f.v;
+}
+
+__device__ __forceinline__ bf16x8 lds_2xb64(const u16* p0, const u16* p1) {
+  Frag f;
+  f.h[0] = *reinterpret_cast<const uint2*>(p0);
+  f.h[1] = *reinterpret_cast<const uint2*>(p1);
+  return f.v;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2 x = {a, b};
+  bf16x2 r = __builtin_convertvector(x, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3,
+                                              float a4, float a5, float a6, float a7) {
+  Frag f;
+  f.u.x = pack_bf16x2(a0, a1);
+  f.u.y = pack_bf16x2(a2, a3);
+  f.u.z = pack_bf16x2(a4, a5);
+  f.u.w = pack_bf16x2(a6, a7);
+  return f.v;
+}
+
+__device__ __forceinline__ uint32_t u16_of(const uint4& v, int e) {
+  uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+  return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float wave_swap32_max(float x) {
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float wave_swap32_sum(float x) {
+  return x + __shfl_xor(x, 32);
+}
+
+}  // namespace dkv

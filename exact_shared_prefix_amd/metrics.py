@@ -1,0 +1,56 @@
+"""Work and traffic accounting for the packed shared-prompt layout.
+
+pairs: number of attended (query, key) pairs per query head under the packed
+mask (prompt rows causal within the prompt; response rows see the whole
+prompt plus their own response causally):
+    pairs = P(P+1)/2 + sum_n [R_n P + R_n(R_n+1)/2]   (PP, RP, RR blocks).
+Useful FLOPs count 4 d per pair forward (two matrix products) and 10 d per pair
+backward (five), times Hq; masked tile waste and recomputation are excluded.
+"""
+from __future__ import annotations
+
+from typing import Sequence
+
+BF16 = 2
+FP32 = 4
+
+
+def pair_blocks(P: int, lengths: Sequence[int]) -> dict:
+    pp = P * (P + 1) // 2
+    rp = sum(int(r) * P for r in lengths)
+    rr = sum(int(r) * (int(r) + 1) // 2 for r in lengths)
+    return {"PP": pp, "RP": rp, "RR": rr, "total": pp + rp + rr}
+
+
+def pairs(P: int, lengths: Sequence[int]) -> int:
+    return pair_blocks(P, lengths)["total"]
+
+
+def replicated_pairs(P: int, lengths: Sequence[int]) -> int:
+    """Pairs of the same batch with the prompt copied into every sequence."""
+    return sum((P + int(r)) * (P + int(r) + 1) // 2 for r in lengths)
+
+
+def useful_flops(P: int, lengths: Sequence[int], Hq: int, d: int) -> dict:
+    n = pairs(P, lengths)
+    return {"fwd": 4 * d * Hq * n, "bwd": 10 * d * Hq * n, "total": 14 * d * Hq * n}
+
+
+def tokens(P: int, lengths: Sequence[int]) -> tuple[int, int]:
+    """(packed, replicated) token counts; their ratio is rho = N(P+R)/(P+NR)."""
+    return P + sum(lengths), sum(P + int(r) for r in lengths)
+
+
+def min_hbm_bytes(P: int, lengths: Sequence[int], Hq: int, Hkv: int, d: int) -> dict:
+    """Compulsory HBM bytes: each input read once, each output written once.
+
+    forward: read q, k, v; write o, lse.
+    backward: read q, k, v, o, dO, lse; write dQ, dK, dV.
+    """
+    T = P + sum(lengths)
+    xq = T * Hq * d * BF16
+    xk = T * Hkv * d * BF16
+    lse = T * Hq * FP32
+    fwd = xq + 2 * xk + xq + lse
+    bwd = 3 * xq + 2 * xk + lse + xq + 2 * xk
+    return {"fwd": fwd, "bwd": bwd, "total": fwd + bwd}

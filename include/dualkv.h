@@ -1,0 +1,101 @@
+/*
+ * dualkv.h -- C ABI of the MI355X (gfx950) shared-prompt attention library.
+ *
+ * The operation (DualKV pages: p1 "Approach", p2 abstract, p3 body): one
+ * micro-batch is packed as a shared prompt of P tokens followed by N
+ * responses, [prompt][resp_0]...[resp_{N-1}], T = P + sum_n R_n tokens instead
+ * of N(P + R). With o_0 = P and o_{n+1} = o_n + R_n, packed row t attends
+ *   A(t) = {0 .. t}                      if t < P        (prompt, causal)
+ *   A(t) = {0 .. P-1} u {o_n .. t}       if o_n <= t < o_{n+1}
+ * i.e. the whole prompt KV region plus its own response region causally. This
+ * is exactly standard attention on the N sequences [prompt; resp_n] with the
+ * prompt computed once; the prompt's dK/dV are summed over all N sequences.
+ *
+ * Conventions for every entry point below:
+ *  - Tensors are device pointers to contiguous row-major arrays, 16-byte
+ *    aligned. bf16 means IEEE bfloat16 (raw 16-bit storage).
+ *      q, o, dO, dQ : [T][Hq][d]  bf16
+ *      k, v, dK, dV : [T][Hkv][d] bf16
+ *      lse          : [Hq][T]     fp32, natural-log log-sum-exp of the scaled
+ *                                 scores of each row (used by the backward)
+ *  - Query head h reads KV head h / (Hq / Hkv) (grouped-query attention);
+ *    Hq must be a multiple of Hkv. Hq == Hkv is plain multi-head attention.
+ *  - Score of (t, j) is softmax_scale * <q_t, k_j>, softmax_scale finite and
+ *    >= 0 (0 gives uniform attention over A(t)).
+ *  - Response lengths: offsets == NULL means N responses of R tokens each.
+ *    Otherwise offsets is a HOST array of N+1 int32 with offsets[0] == P,
+ *    offsets non-decreasing and offsets[N] == T (R is ignored). Empty
+ *    responses (R_n = 0) and P == 0 (the replicated, unshared layout) are
+ *    allowed.
+ *  - Supported head_dim d: 64, 128. T * max(Hq, Hkv) * d must stay below 2^31.
+ *  - Ownership: the caller owns every buffer, including the workspace; the
+ *    library allocates no device memory and keeps no state between calls.
+ *    Outputs are overwritten, never accumulated into.
+ *  - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL is the null
+ *    stream) and the call returns without waiting for the device. The small
+ *    work list is uploaded into the workspace with a host-to-device copy on
+ *    the same stream. Two calls that share a workspace must be ordered.
+ *  - Errors: arguments are checked before any HIP call. DUALKV_ERR_INVALID_ARG
+ *    for bad shapes, offsets, pointers, alignment or scale;
+ *    DUALKV_ERR_UNSUPPORTED for a head_dim or mode not built;
+ *    DUALKV_ERR_WORKSPACE if workspace_bytes is below the *_workspace_bytes
+ *    figure; DUALKV_ERR_HIP if a HIP call or kernel launch fails. Nothing is
+ *    printed and no exception crosses the ABI. On error no output is written
+ *    unless the error is DUALKV_ERR_HIP.
+ */
+#ifndef DUALKV_H
+#define DUALKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DUALKV_OK = 0,
+  DUALKV_ERR_INVALID_ARG = 1,
+  DUALKV_ERR_UNSUPPORTED = 2,
+  DUALKV_ERR_WORKSPACE = 3,
+  DUALKV_ERR_HIP = 4
+} dualkv_status;
+
+/* Workspace (device bytes) dualkv_fwd needs for this problem; 0 if the
+ * arguments are invalid. Pure host computation. */
+size_t dualkv_fwd_workspace_bytes(int P, int R, int N, const int32_t* offsets,
+                                  int Hq, int Hkv, int d);
+
+/* Workspace dualkv_bwd needs: the work list, D = rowsum(dO*O) [Hq][T] fp32
+ * and fp32 accumulators for dQ [T][Hq][d], dK and dV [T][Hkv][d].
+ * 0 if the arguments are invalid. */
+size_t dualkv_bwd_workspace_bytes(int P, int R, int N, const int32_t* offsets,
+                                  int Hq, int Hkv, int d, int deterministic);
+
+/* Forward pass (DualKV pages, p1 "Approach" / p2 abstract: one launch that
+ * walks the prompt KV region and then the row's own response KV region).
+ * Reads q, k, v; writes o (bf16) and lse (fp32, natural log). */
+dualkv_status dualkv_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int P, int R, int N, const int32_t* offsets,
+                         int Hq, int Hkv, int d, float softmax_scale,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward pass of L = sum_t <dO_t, O_t> (p1 "Approach": gradients of the
+ * shared prompt accumulated across all N sequences with fp32 atomics).
+ * Reads q, k, v, o, lse (from dualkv_fwd on the same inputs) and dO; writes
+ * dQ, dK, dV (bf16). deterministic must be 0: the reproducible-order
+ * reduction mode is not built and returns DUALKV_ERR_UNSUPPORTED. */
+dualkv_status dualkv_bwd(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dO, void* dQ, void* dK, void* dV,
+                         int P, int R, int N, const int32_t* offsets,
+                         int Hq, int Hkv, int d, float softmax_scale, int deterministic,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static English description of a status code (never NULL). */
+const char* dualkv_status_string(dualkv_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DUALKV_H */

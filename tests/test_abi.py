@@ -1,0 +1,132 @@
+"""The C-ABI library builds, loads, exports what include/dualkv.h declares and
+rejects bad arguments before touching the GPU (no compute calls here: every
+call below fails argument checks, so no HIP API is reached)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_shared_prefix_amd import binding, metrics
+from exact_shared_prefix_amd.binding import (ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, OK,
+                                             Packing)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dualkv.h")
+FAKE = 0x100000  # aligned, never dereferenced: every call here fails validation first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dualkv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_symbols() == sorted(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    nm = os.popen(f"nm -D --defined-only {binding.LIB_PATH}").read()
+    for name in declared_symbols():
+        assert re.search(rf"\bT {name}\b", nm), name
+
+
+def test_library_has_gfx950_code_object():
+    data = open(binding.LIB_PATH, "rb").read()
+    assert b"gfx950" in data
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert binding.status_string(s)
+    assert binding.status_string(99) == "unknown status"
+
+
+def _fwd(lib, P=16, R=8, N=2, offsets=None, Hq=4, Hkv=2, d=128, scale=0.1, ws=FAKE,
+         ws_bytes=1 << 20, q=FAKE, lse=FAKE):
+    offp = None
+    if offsets is not None:
+        arr = (ctypes.c_int32 * len(offsets))(*offsets)
+        offp = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+    return lib.dualkv_fwd(q, FAKE, FAKE, FAKE, lse, P, R, N, offp, Hq, Hkv, d, scale, ws,
+                          ws_bytes, None)
+
+
+def _bwd(lib, P=16, R=8, N=2, Hq=4, Hkv=2, d=128, scale=0.1, det=0, ws=FAKE, ws_bytes=1 << 20,
+         dq=FAKE):
+    return lib.dualkv_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dq, FAKE, FAKE, P, R, N, None, Hq,
+                          Hkv, d, scale, det, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=0), ERR_INVALID_ARG),
+    (dict(P=-1), ERR_INVALID_ARG),
+    (dict(R=-3), ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=4), ERR_INVALID_ARG),
+    (dict(Hkv=0), ERR_INVALID_ARG),
+    (dict(d=96), ERR_UNSUPPORTED),
+    (dict(d=256), ERR_UNSUPPORTED),
+    (dict(scale=-1.0), ERR_INVALID_ARG),
+    (dict(scale=float("nan")), ERR_INVALID_ARG),
+    (dict(scale=float("inf")), ERR_INVALID_ARG),
+    (dict(q=None), ERR_INVALID_ARG),
+    (dict(q=FAKE + 2), ERR_INVALID_ARG),          # misaligned
+    (dict(lse=None), ERR_INVALID_ARG),
+    (dict(offsets=[15, 20, 30], N=2), ERR_INVALID_ARG),  # offsets[0] != P
+    (dict(offsets=[16, 30, 20], N=2), ERR_INVALID_ARG),  # decreasing
+    (dict(R=1 << 12, N=1 << 20), ERR_INVALID_ARG),  # T >= 2^31
+    (dict(P=1 << 22, Hq=32, Hkv=8, d=128, R=0), ERR_INVALID_ARG),  # T*Hq*d >= 2^31
+    (dict(ws=None), ERR_WORKSPACE),
+    (dict(ws_bytes=1), ERR_WORKSPACE),
+])
+def test_fwd_rejects_bad_arguments(lib, kw, status):
+    assert _fwd(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(det=1), ERR_UNSUPPORTED),
+    (dict(N=0), ERR_INVALID_ARG),
+    (dict(Hq=3, Hkv=2), ERR_INVALID_ARG),
+    (dict(d=32), ERR_UNSUPPORTED),
+    (dict(scale=-0.5), ERR_INVALID_ARG),
+    (dict(dq=None), ERR_INVALID_ARG),
+    (dict(dq=FAKE + 8), ERR_INVALID_ARG),
+    (dict(ws_bytes=16), ERR_WORKSPACE),
+])
+def test_bwd_rejects_bad_arguments(lib, kw, status):
+    assert _bwd(lib, **kw) == status
+
+
+def test_workspace_sizes(lib):
+    pk = Packing(128, R=64, N=4)
+    nf = binding.fwd_workspace_bytes(pk, 4, 2, 64)
+    nb = binding.bwd_workspace_bytes(pk, 4, 2, 64)
+    assert nf >= 16 and nf % 256 == 0
+    T = pk.T
+    # bwd holds at least D [Hq,T] and fp32 dQ/dK/dV accumulators
+    assert nb >= 4 * (4 * T + T * 4 * 64 + 2 * T * 2 * 64)
+    with pytest.raises(binding.DualKVError):
+        binding.bwd_workspace_bytes(pk, 4, 2, 64, deterministic=True)
+    with pytest.raises(binding.DualKVError):
+        binding.fwd_workspace_bytes(pk, 4, 3, 64)
+    # ragged offsets are accepted and size like the uniform case of equal T
+    rag = Packing(128, lengths=[10, 100, 0, 146])
+    assert binding.fwd_workspace_bytes(rag, 4, 2, 64) > 0
+    assert not rag.uniform and pk.uniform
+
+
+def test_pair_accounting_matches_brute_force():
+    from oracle import attended_keys
+    for P, lengths in ((5, [3, 0, 4]), (0, [6, 2]), (9, [1])):
+        brute = sum(len(attended_keys(t, P, lengths)) for t in range(P + sum(lengths)))
+        assert metrics.pairs(P, lengths) == brute
+        rep = sum(sum(range(1, P + r + 1)) for r in lengths)
+        assert metrics.replicated_pairs(P, lengths) == rep
