@@ -1,0 +1,342 @@
+#!/usr/bin/env python3
+"""Forward + backward throughput of packed shared-prompt attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = dualkv_fwd + dualkv_bwd (all of its phases) over the packed batch
+[prompt P][N responses], inputs resident in HBM before the timed region.
+Prints one JSON line on stdout (progress goes to stderr):
+
+* value: useful TFLOP/s, 14 d Hq pairs per step (pairs = attended (query, key)
+  pairs under the packed mask; masked tile waste and recomputation excluded)
+  divided by the measured time per step;
+* roofline: the dominant kernel (largest share of the step) timed with HIP
+  events on the launch stream, its algorithmic FLOPs per launch against the
+  MI355X dense bf16 MFMA peak; traffic from committed rocprofv3 counters when
+  they were taken on the current kernel source, else null;
+* replicated: the same kernels on the unshared layout (P = 0, N sequences of
+  P + R_n tokens) and the packed speed-up over it;
+* cpu_baseline: the float64 CPU oracle timed on a bounded sample of the same
+  workload on the host's cores, scaled to the whole workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+METRIC = "fwd+bwd useful TFLOP/s and % bf16 MFMA peak at P=8K,R=4K,N=32"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "main_kernel": ["exact_shared_prefix_amd/csrc/bwd.hip", "exact_shared_prefix_amd/csrc/common.h"],
+    "fwd_kernel": ["exact_shared_prefix_amd/csrc/fwd.hip", "exact_shared_prefix_amd/csrc/common.h"],
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest(kernel: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    counters, if they were taken on the current source of the kernel."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None, "no counters committed"
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != source_digest(kernel):
+        return None, "kernel changed since the counters were taken"
+    return float(rec["hbm_bytes_per_launch"]), path
+
+
+def replicated_inputs(q, k, v, do, P, lengths):
+    import torch
+    offs = [P]
+    for r in lengths:
+        offs.append(offs[-1] + r)
+    idx = torch.cat([torch.cat([torch.arange(0, P), torch.arange(offs[n], offs[n + 1])])
+                     for n in range(len(lengths))]).to(q.device)
+    return (q.index_select(0, idx), k.index_select(0, idx), v.index_select(0, idx),
+            do.index_select(0, idx), [P + r for r in lengths])
+
+
+def time_steps(q, k, v, do, pk, scale, steps, warmup, phase_events=True):
+    """Run warmup + timed fwd+bwd steps; returns timings in ms."""
+    import torch
+    from exact_shared_prefix_amd import binding
+    dev = q.device
+    Hq, d = q.shape[1], q.shape[2]
+    Hkv = k.shape[1]
+    o = torch.empty_like(q)
+    lse = torch.empty((Hq, pk.T), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    wsf = torch.empty(binding.fwd_workspace_bytes(pk, Hq, Hkv, d), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(binding.bwd_workspace_bytes(pk, Hq, Hkv, d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        binding.fwd(q, k, v, pk, scale, out=o, lse=lse, workspace=wsf)
+        if ev:
+            ev[1].record(stream)
+        binding.bwd(q, k, v, o, lse, do, pk, scale, dq, dk, dv, workspace=wsb,
+                    phases=binding.PHASE_PRE)
+        if ev:
+            ev[2].record(stream)
+        binding.bwd(q, k, v, o, lse, do, pk, scale, dq, dk, dv, workspace=wsb,
+                    phases=binding.PHASE_MAIN)
+        if ev:
+            ev[3].record(stream)
+        binding.bwd(q, k, v, o, lse, do, pk, scale, dq, dk, dv, workspace=wsb,
+                    phases=binding.PHASE_FINISH)
+        if ev:
+            ev[4].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_all0.record(stream)
+    for i in range(steps):
+        step(evs[i] if phase_events else None)
+    t_all1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - wall0) * 1e3
+    total = t_all0.elapsed_time(t_all1)
+    res = {"ms_per_step": total / steps, "wall_ms_per_step": wall / steps}
+    if phase_events:
+        def avg(a, b):
+            return sum(e[a].elapsed_time(e[b]) for e in evs) / steps
+        res.update(fwd_ms=avg(0, 1), bwd_pre_ms=avg(1, 2), bwd_main_ms=avg(2, 3),
+                   bwd_finish_ms=avg(3, 4), bwd_ms=avg(1, 4))
+    del o, lse, dq, dk, dv, wsf, wsb
+    return res
+
+
+def cpu_baseline(inp, budget_s: float) -> dict:
+    """The float64 oracle on a bounded sample: whole replicated sequences
+    (prompt + response n) for single query heads, fwd + bwd, until about
+    budget_s of CPU work; scaled by pair counts to the whole workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from exact_shared_prefix_amd import metrics
+    from oracle.replicated import causal_attention_bwd, causal_attention_fwd
+
+    cores = len(os.sched_getaffinity(0))
+    P, L = inp.P, inp.lengths
+    offs = [P]
+    for r in L:
+        offs.append(offs[-1] + r)
+    G = inp.Hq // inp.Hkv
+    done_pairs, t_used, samples = 0, 0.0, []
+    with threadpool_limits(cores):
+        threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+        order = [(n, h) for h in range(inp.Hq) for n in range(len(L))]
+        for n, h in order:
+            a, b = offs[n], offs[n + 1]
+            sl = np.r_[0:P, a:b]
+            qh = inp.q[sl, h].float().numpy().astype(np.float64)
+            kh = inp.k[sl, h // G].float().numpy().astype(np.float64)
+            vh = inp.v[sl, h // G].float().numpy().astype(np.float64)
+            dh = inp.do[sl, h].float().numpy().astype(np.float64)
+            t0 = time.perf_counter()
+            causal_attention_fwd(qh, kh, vh, inp.scale)
+            causal_attention_bwd(qh, kh, vh, dh, inp.scale)
+            t_used += time.perf_counter() - t0
+            Ln = P + (b - a)
+            done_pairs += Ln * (Ln + 1) // 2
+            samples.append((n, h, Ln))
+            if t_used >= budget_s:
+                break
+    total_pairs = metrics.replicated_pairs(P, L) * inp.Hq
+    est_s = t_used * total_pairs / done_pairs
+    useful = metrics.useful_flops(P, L, inp.Hq, inp.d)["total"]
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next(ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    return {
+        "value": useful / est_s / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{len(samples)} replicated sequence(s) x query head (first: response "
+                   f"{samples[0][0]}, head {samples[0][1]}, {samples[0][2]} tokens), textbook "
+                   f"float64 fwd+bwd in {t_used:.1f} s; whole workload extrapolated by replicated "
+                   f"pair count ({est_s:.0f} s)"),
+        "cpu_model": model,
+        "seconds_measured": t_used,
+        "seconds_extrapolated": est_s,
+    }
+
+
+def calibrate_copy(nbytes: int) -> None:
+    """A plain device copy of known size, for scaling HBM byte counters."""
+    import torch
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": x.numel() * 4, "copy_bytes_written": y.numel() * 4}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-replicated", action="store_true", help="skip the unshared-layout run")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        return 2
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return 0
+
+    import torch
+
+    from exact_shared_prefix_amd import binding, metrics
+    from exact_shared_prefix_amd.inputs import HEADLINE, WORKLOADS, workload_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    binding.load()
+    name = args.workload or HEADLINE
+    w = WORKLOADS[name]
+    log(f"[bench] workload {name}: generating seeded inputs")
+    inp = workload_inputs(w)
+    P, L = inp.P, inp.lengths
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    torch.empty(1, device=dev)  # initialise the caching allocator before resetting its stats
+    torch.cuda.reset_peak_memory_stats(dev)
+    q, k, v, do = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.do))
+    pk = binding.Packing(P, L)
+    flops = metrics.useful_flops(P, L, inp.Hq, inp.d)
+    pairs = metrics.pairs(P, L)
+
+    log(f"[bench] packed T={inp.T}: {args.warmup} warmup + {args.steps} timed steps")
+    packed = time_steps(q, k, v, do, pk, inp.scale, args.steps, args.warmup)
+    torch.cuda.synchronize()
+    peak_packed = torch.cuda.max_memory_allocated(dev)
+    ms = packed["ms_per_step"]
+    value = flops["total"] / (ms * 1e-3) / 1e12
+    log(f"[bench] packed: {ms:.2f} ms/step, {value:.1f} useful TFLOP/s "
+        f"(fwd {packed['fwd_ms']:.2f} ms, bwd {packed['bwd_ms']:.2f} ms, main {packed['bwd_main_ms']:.2f} ms)")
+
+    kernels = {
+        "fwd_kernel": {"ms": packed["fwd_ms"], "flops": flops["fwd"]},
+        "main_kernel": {"ms": packed["bwd_main_ms"], "flops": flops["bwd"]},
+    }
+    dom = max(kernels, key=lambda n: kernels[n]["ms"])
+    ach = kernels[dom]["flops"] / (kernels[dom]["ms"] * 1e-3) / 1e12
+    traffic, traffic_src = stored_traffic(dom, name)
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": traffic,
+                "traffic_source": traffic_src,
+                "algorithmic_flop_per_launch": kernels[dom]["flops"],
+                "avg_launch_ms": kernels[dom]["ms"]}
+    other = {n: {"ms": kv["ms"], "tflops": kv["flops"] / (kv["ms"] * 1e-3) / 1e12}
+             for n, kv in kernels.items()}
+
+    replicated = None
+    if not args.no_replicated:
+        del q, k, v, do
+        torch.cuda.empty_cache()
+        qh, kh, vh, dh = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.do))
+        rq, rk, rv, rd, rlen = replicated_inputs(qh, kh, vh, dh, P, L)
+        del qh, kh, vh, dh
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats(dev)
+        rsteps = max(2, args.steps // 2)
+        log(f"[bench] replicated layout T={rq.shape[0]}: 1 warmup + {rsteps} timed steps")
+        try:
+            rep = time_steps(rq, rk, rv, rd, binding.Packing(0, rlen), inp.scale, rsteps, 1,
+                             phase_events=False)
+            rflops = metrics.useful_flops(0, rlen, inp.Hq, inp.d)["total"]
+            replicated = {"ms_per_step": rep["ms_per_step"],
+                          "tflops_on_own_pairs": rflops / (rep["ms_per_step"] * 1e-3) / 1e12,
+                          "speedup_packed_over_replicated": rep["ms_per_step"] / ms,
+                          "tokens": int(rq.shape[0]),
+                          "peak_hbm_gb": torch.cuda.max_memory_allocated(dev) / 1e9}
+            log(f"[bench] replicated: {rep['ms_per_step']:.2f} ms/step -> packed speed-up "
+                f"{replicated['speedup_packed_over_replicated']:.2f}x")
+        except torch.cuda.OutOfMemoryError:
+            replicated = {"status": "out of memory"}
+        del rq, rk, rv, rd
+
+    cpu = None
+    if not args.no_cpu:
+        log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
+        cpu = cpu_baseline(inp, args.cpu_seconds)
+        log(f"[bench] CPU oracle: {cpu['value']:.4g} TFLOP/s on {cpu['cores']} threads")
+
+    packed_tok, rep_tok = metrics.tokens(P, L)
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded i.i.d. normal bf16 q/k/v/dO",
+        "frac_of_peak": value / PEAK_BF16_TFLOPS,
+        "config": {"workload": name, "P": P, "N": len(L),
+                   "R": L[0] if len(set(L)) == 1 else "ragged", "lengths_sum": sum(L),
+                   "Hq": inp.Hq, "Hkv": inp.Hkv, "head_dim": inp.d,
+                   "packed_tokens": packed_tok, "replicated_tokens": rep_tok,
+                   "pairs_per_head": pairs, "useful_tflop_per_step": flops["total"] / 1e12,
+                   "parallelism": "single GPU"},
+        "timing_ms": {kk: round(vv, 4) for kk, vv in packed.items()},
+        "kernels": other,
+        "roofline": roofline,
+        "peak_hbm_gb": peak_packed / 1e9,
+        "replicated": replicated,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

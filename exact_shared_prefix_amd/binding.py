@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_PKG, "libdualkv.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 EXPORTS = ("dualkv_fwd_workspace_bytes", "dualkv_bwd_workspace_bytes", "dualkv_fwd",
-           "dualkv_bwd", "dualkv_status_string")
+           "dualkv_bwd", "dualkv_bwd_phases", "dualkv_status_string")
+PHASE_PRE, PHASE_MAIN, PHASE_FINISH, PHASE_ALL = 1, 2, 4, 7
 
 _lib = None
 
@@ -50,6 +51,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dualkv_bwd.restype = c_int
     lib.dualkv_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, c_int, c_int, c_int, i32p,
                                c_int, c_int, c_int, c_float, c_int, vp, c_size, vp]
+    lib.dualkv_bwd_phases.restype = c_int
+    lib.dualkv_bwd_phases.argtypes = lib.dualkv_bwd.argtypes + [c_int]
     lib.dualkv_status_string.restype = ctypes.c_char_p
     lib.dualkv_status_string.argtypes = [c_int]
     _lib = lib
@@ -84,6 +87,7 @@ class Packing:
             offs.append(offs[-1] + x)
         self.T = offs[-1]
         self._offsets = (ctypes.c_int32 * (self.N + 1))(*offs)
+        self._ws = {}  # workspace sizes already asked of the library
 
     def offsets_ptr(self):
         if self.uniform:
@@ -112,15 +116,23 @@ def _check_tensor(name, t, shape, dtype, device):
 
 
 def fwd_workspace_bytes(pk: Packing, Hq: int, Hkv: int, d: int) -> int:
+    key = ("fwd", Hq, Hkv, d)
+    if key in pk._ws:
+        return pk._ws[key]
     n = load().dualkv_fwd_workspace_bytes(pk.P, pk.R, pk.N, pk.offsets_ptr(), Hq, Hkv, d)
+    pk._ws[key] = n
     if n == 0:
         raise DualKVError(ERR_INVALID_ARG, "invalid problem shape")
     return n
 
 
 def bwd_workspace_bytes(pk: Packing, Hq: int, Hkv: int, d: int, deterministic: bool = False) -> int:
+    key = ("bwd", Hq, Hkv, d, bool(deterministic))
+    if key in pk._ws:
+        return pk._ws[key]
     n = load().dualkv_bwd_workspace_bytes(pk.P, pk.R, pk.N, pk.offsets_ptr(), Hq, Hkv, d,
                                           int(deterministic))
+    pk._ws[key] = n
     if n == 0:
         raise DualKVError(ERR_UNSUPPORTED if deterministic else ERR_INVALID_ARG,
                           "invalid problem shape or unsupported mode")
@@ -156,8 +168,13 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pk: Packing,
 
 
 def bwd(q, k, v, o, lse, do, pk: Packing, scale: Optional[float] = None,
-        dq=None, dk=None, dv=None, workspace=None, deterministic: bool = False, stream=None):
-    """dualkv_bwd -> (dq, dk, dv), bf16, same layouts as q, k, v."""
+        dq=None, dk=None, dv=None, workspace=None, deterministic: bool = False, stream=None,
+        phases: int = PHASE_ALL):
+    """dualkv_bwd -> (dq, dk, dv), bf16, same layouts as q, k, v.
+
+    phases selects a subset of the backward's stream-ordered phases
+    (dualkv_bwd_phases); the outputs are complete only once all three ran, in
+    order, on the same workspace."""
     T, Hq, d = q.shape
     Hkv = k.shape[1]
     dev = q.device
@@ -172,10 +189,13 @@ def bwd(q, k, v, o, lse, do, pk: Packing, scale: Optional[float] = None,
     nws = bwd_workspace_bytes(pk, Hq, Hkv, d, deterministic)
     if workspace is None or workspace.numel() < nws:
         workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
-    _check(load().dualkv_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
-                             _ptr(dk), _ptr(dv), pk.P, pk.R, pk.N, pk.offsets_ptr(), Hq, Hkv, d,
-                             float(scale), int(deterministic), _ptr(workspace), workspace.numel(),
-                             _stream_ptr(stream)))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
+            pk.P, pk.R, pk.N, pk.offsets_ptr(), Hq, Hkv, d, float(scale), int(deterministic),
+            _ptr(workspace), workspace.numel(), _stream_ptr(stream))
+    if phases == PHASE_ALL:
+        _check(load().dualkv_bwd(*args))
+    else:
+        _check(load().dualkv_bwd_phases(*args, int(phases)))
     return dq, dk, dv
 
 

@@ -3,9 +3,12 @@
 // The packed layout is the DualKV one (p2 abstract: P + NR tokens per
 // micro-batch; p1 "Approach": a shared-context KV region and per-sequence
 // response KV regions). Work lists are built on the host and copied into the
-// caller's workspace on the caller's stream; nothing is allocated here.
+// caller's workspace on the caller's stream through pinned staging buffers;
+// no device memory is allocated here.
 #include <algorithm>
 #include <cmath>
+#include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/dualkv.h"
@@ -17,7 +20,8 @@ hipError_t launch_fwd(const Problem& pb, const void* q, const void* k, const voi
 hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dO, void* dQ, void* dK,
                       void* dV, const BwdItem* items_dev, int n_items, float* delta,
-                      float* dq_acc, float* dk_acc, float* dv_acc, hipStream_t stream);
+                      float* dq_acc, float* dk_acc, float* dv_acc, hipStream_t stream,
+                      int phase_mask);
 }  // namespace dkv
 
 using namespace dkv;
@@ -61,6 +65,59 @@ dualkv_status check_shape(int P, int R, int N, const int32_t* offsets, int Hq, i
 }
 
 bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Work-list upload. A copy from pageable host memory may wait for the stream
+// to drain, which would leave the GPU idle between launches, so lists are
+// staged through a small ring of pinned host buffers per device. A slot is
+// reused only after the event recorded behind its previous copy completed.
+class Staging {
+ public:
+  hipError_t upload(void* dst, const void* src, size_t n, hipStream_t stream) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu_);
+    Slot& sl = ring_[dev][next_[dev]];
+    next_[dev] = (next_[dev] + 1) % kSlots;
+    if (sl.pending) {
+      if ((e = hipEventSynchronize(sl.ev)) != hipSuccess) return e;
+      sl.pending = false;
+    }
+    if (!sl.ev && (e = hipEventCreateWithFlags(&sl.ev, hipEventDisableTiming)) != hipSuccess)
+      return e;
+    if (sl.cap < n) {
+      if (sl.host && (e = hipHostFree(sl.host)) != hipSuccess) return e;
+      sl.host = nullptr;
+      sl.cap = 0;
+      const size_t cap = std::max<size_t>(n, 64 << 10);
+      if ((e = hipHostMalloc(&sl.host, cap, hipHostMallocDefault)) != hipSuccess) return e;
+      sl.cap = cap;
+    }
+    std::memcpy(sl.host, src, n);
+    if ((e = hipMemcpyAsync(dst, sl.host, n, hipMemcpyHostToDevice, stream)) != hipSuccess) return e;
+    if ((e = hipEventRecord(sl.ev, stream)) != hipSuccess) return e;
+    sl.pending = true;
+    return hipSuccess;
+  }
+
+ private:
+  static constexpr int kDevices = 16, kSlots = 8;
+  struct Slot {
+    void* host = nullptr;
+    size_t cap = 0;
+    hipEvent_t ev = nullptr;
+    bool pending = false;
+  };
+  std::mutex mu_;
+  Slot ring_[kDevices][kSlots];
+  int next_[kDevices] = {};
+};
+
+hipError_t upload(void* dst, const void* src, size_t n, hipStream_t stream) {
+  static Staging* staging = new Staging();  // process lifetime, never torn down
+  return staging->upload(dst, src, n, stream);
+}
 
 // Forward work list: 128-row query tiles that never straddle a segment,
 // longest (most keys) first so the tail of the grid is short.
@@ -156,8 +213,7 @@ dualkv_status dualkv_fwd(const void* q, const void* k, const void* v, void* o, f
   if (!aligned16(workspace)) return DUALKV_ERR_INVALID_ARG;
   if (items.empty()) return DUALKV_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (hipMemcpyAsync(workspace, items.data(), items.size() * sizeof(FwdItem), hipMemcpyHostToDevice,
-                     s) != hipSuccess)
+  if (upload(workspace, items.data(), items.size() * sizeof(FwdItem), s) != hipSuccess)
     return DUALKV_ERR_HIP;
   if (launch_fwd(pb, q, k, v, o, lse, static_cast<const FwdItem*>(workspace), (int)items.size(),
                  s) != hipSuccess)
@@ -165,14 +221,15 @@ dualkv_status dualkv_fwd(const void* q, const void* k, const void* v, void* o, f
   return DUALKV_OK;
 }
 
-dualkv_status dualkv_bwd(const void* q, const void* k, const void* v, const void* o,
-                         const float* lse, const void* dO, void* dQ, void* dK, void* dV, int P,
-                         int R, int N, const int32_t* offsets, int Hq, int Hkv, int d,
-                         float softmax_scale, int deterministic, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+dualkv_status dualkv_bwd_phases(const void* q, const void* k, const void* v, const void* o,
+                                const float* lse, const void* dO, void* dQ, void* dK, void* dV,
+                                int P, int R, int N, const int32_t* offsets, int Hq, int Hkv,
+                                int d, float softmax_scale, int deterministic, void* workspace,
+                                size_t workspace_bytes, void* stream, int phase_mask) {
   Problem pb;
   dualkv_status st = check_shape(P, R, N, offsets, Hq, Hkv, d, pb);
   if (st != DUALKV_OK) return st;
+  if (phase_mask < 1 || phase_mask > 7) return DUALKV_ERR_INVALID_ARG;
   if (deterministic) return DUALKV_ERR_UNSUPPORTED;
   if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return DUALKV_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
@@ -186,16 +243,24 @@ dualkv_status dualkv_bwd(const void* q, const void* k, const void* v, const void
   if (pb.T == 0) return DUALKV_OK;
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (!items.empty() &&
-      hipMemcpyAsync(ws + L.items, items.data(), items.size() * sizeof(BwdItem),
-                     hipMemcpyHostToDevice, s) != hipSuccess)
+  if ((phase_mask & 2) && !items.empty() &&
+      upload(ws + L.items, items.data(), items.size() * sizeof(BwdItem), s) != hipSuccess)
     return DUALKV_ERR_HIP;
   if (launch_bwd(pb, q, k, v, o, lse, dO, dQ, dK, dV, reinterpret_cast<const BwdItem*>(ws + L.items),
                  (int)items.size(), reinterpret_cast<float*>(ws + L.delta),
                  reinterpret_cast<float*>(ws + L.dq), reinterpret_cast<float*>(ws + L.dk),
-                 reinterpret_cast<float*>(ws + L.dv), s) != hipSuccess)
+                 reinterpret_cast<float*>(ws + L.dv), s, phase_mask) != hipSuccess)
     return DUALKV_ERR_HIP;
   return DUALKV_OK;
+}
+
+dualkv_status dualkv_bwd(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dO, void* dQ, void* dK, void* dV, int P,
+                         int R, int N, const int32_t* offsets, int Hq, int Hkv, int d,
+                         float softmax_scale, int deterministic, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return dualkv_bwd_phases(q, k, v, o, lse, dO, dQ, dK, dV, P, R, N, offsets, Hq, Hkv, d,
+                           softmax_scale, deterministic, workspace, workspace_bytes, stream, 7);
 }
 
 const char* dualkv_status_string(dualkv_status s) {

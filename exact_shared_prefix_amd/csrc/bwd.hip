@@ -308,10 +308,11 @@ static int stream_grid(size_t n4) {
 hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dO, void* dQ, void* dK,
                       void* dV, const BwdItem* items_dev, int n_items, float* delta,
-                      float* dq_acc, float* dk_acc, float* dv_acc, hipStream_t stream) {
+                      float* dq_acc, float* dk_acc, float* dv_acc, hipStream_t stream,
+                      int phase_mask) {
   const size_t nq = (size_t)pb.T * pb.Hq * pb.d, nk = (size_t)pb.T * pb.Hkv * pb.d;
   // 1. D and zeroed accumulators
-  {
+  if (phase_mask & 1) {
     const long long lanes = (long long)pb.T * pb.Hq * (pb.d / 8);
     dim3 grid((unsigned)((lanes + 255) / 256));
     if (pb.d == 128)
@@ -328,7 +329,7 @@ hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const voi
                        (float4*)dv_acc, nk / 4);
   }
   // 2. main
-  if (n_items > 0) {
+  if ((phase_mask & 2) && n_items > 0) {
     HeadMap hm = make_headmap(n_items, pb.Hkv);
     dim3 grid(headmap_grid(hm));
     const float c = pb.scale * kLog2e;
@@ -342,12 +343,14 @@ hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const voi
                          dk_acc, dv_acc, items_dev, hm, pb.T, pb.Hq, pb.Hkv, c);
   }
   // 3. convert
-  hipLaunchKernelGGL(convert_kernel, dim3(stream_grid(nq / 4)), dim3(256), 0, stream,
-                     (const float4*)dq_acc, (uint2*)dQ, nq / 4, pb.scale);
-  hipLaunchKernelGGL(convert_kernel, dim3(stream_grid(nk / 4)), dim3(256), 0, stream,
-                     (const float4*)dk_acc, (uint2*)dK, nk / 4, pb.scale);
-  hipLaunchKernelGGL(convert_kernel, dim3(stream_grid(nk / 4)), dim3(256), 0, stream,
-                     (const float4*)dv_acc, (uint2*)dV, nk / 4, 1.0f);
+  if (phase_mask & 4) {
+    hipLaunchKernelGGL(convert_kernel, dim3(stream_grid(nq / 4)), dim3(256), 0, stream,
+                       (const float4*)dq_acc, (uint2*)dQ, nq / 4, pb.scale);
+    hipLaunchKernelGGL(convert_kernel, dim3(stream_grid(nk / 4)), dim3(256), 0, stream,
+                       (const float4*)dk_acc, (uint2*)dK, nk / 4, pb.scale);
+    hipLaunchKernelGGL(convert_kernel, dim3(stream_grid(nk / 4)), dim3(256), 0, stream,
+                       (const float4*)dv_acc, (uint2*)dV, nk / 4, 1.0f);
+  }
   return hipGetLastError();
 }
 

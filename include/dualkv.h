@@ -28,13 +28,16 @@
  *    responses (R_n = 0) and P == 0 (the replicated, unshared layout) are
  *    allowed.
  *  - Supported head_dim d: 64, 128. T * max(Hq, Hkv) * d must stay below 2^31.
- *  - Ownership: the caller owns every buffer, including the workspace; the
- *    library allocates no device memory and keeps no state between calls.
- *    Outputs are overwritten, never accumulated into.
+ *  - Ownership: the caller owns every device buffer, including the
+ *    workspace; the library allocates no device memory. Its only state is a
+ *    small ring of pinned host staging buffers (grown on demand, kept for the
+ *    life of the process) used to upload work lists. Outputs are overwritten,
+ *    never accumulated into.
  *  - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL is the null
  *    stream) and the call returns without waiting for the device. The small
- *    work list is uploaded into the workspace with a host-to-device copy on
- *    the same stream. Two calls that share a workspace must be ordered.
+ *    work list is uploaded into the workspace with an asynchronous
+ *    host-to-device copy on the same stream. Two calls that share a workspace
+ *    must be ordered. Calls are thread-safe.
  *  - Errors: arguments are checked before any HIP call. DUALKV_ERR_INVALID_ARG
  *    for bad shapes, offsets, pointers, alignment or scale;
  *    DUALKV_ERR_UNSUPPORTED for a head_dim or mode not built;
@@ -90,6 +93,20 @@ dualkv_status dualkv_bwd(const void* q, const void* k, const void* v, const void
                          int P, int R, int N, const int32_t* offsets,
                          int Hq, int Hkv, int d, float softmax_scale, int deterministic,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* The backward of dualkv_bwd split into its three stream-ordered phases, so a
+ * caller can time or interleave them: bit 1 = preprocess (D = rowsum(dO*O),
+ * zeroed fp32 accumulators in the workspace), bit 2 = main (the two-region
+ * KV-stationary pass, atomics into the accumulators), bit 4 = finish (fp32
+ * accumulators -> bf16 dQ, dK, dV). Same arguments and checks as dualkv_bwd;
+ * dualkv_bwd is phase_mask 7. Phases must run in order on the same workspace
+ * with the same arguments; a mask of 0 or above 7 is DUALKV_ERR_INVALID_ARG. */
+dualkv_status dualkv_bwd_phases(const void* q, const void* k, const void* v, const void* o,
+                                const float* lse, const void* dO, void* dQ, void* dK, void* dV,
+                                int P, int R, int N, const int32_t* offsets,
+                                int Hq, int Hkv, int d, float softmax_scale, int deterministic,
+                                void* workspace, size_t workspace_bytes, void* stream,
+                                int phase_mask);
 
 /* Static English description of a status code (never NULL). */
 const char* dualkv_status_string(dualkv_status s);

@@ -105,6 +105,14 @@ def test_bwd_rejects_bad_arguments(lib, kw, status):
     assert _bwd(lib, **kw) == status
 
 
+@pytest.mark.parametrize("mask,status", [(0, ERR_INVALID_ARG), (8, ERR_INVALID_ARG),
+                                         (-1, ERR_INVALID_ARG), (2, ERR_WORKSPACE)])
+def test_bwd_phases_rejects_bad_mask(lib, mask, status):
+    r = lib.dualkv_bwd_phases(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 8, 2, None,
+                              4, 2, 128, 0.1, 0, FAKE, 16, None, mask)
+    assert r == status
+
+
 def test_workspace_sizes(lib):
     pk = Packing(128, R=64, N=4)
     nf = binding.fwd_workspace_bytes(pk, 4, 2, 64)
