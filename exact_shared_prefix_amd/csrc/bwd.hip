@@ -62,19 +62,29 @@ __global__ __launch_bounds__(256) void zero_kernel(float4* __restrict__ p, size_
 }
 
 // ------------------------------------------------------------------ main --
-template <int D>
-__global__ __launch_bounds__(256, 1) void main_kernel(
+// Column position of query q (0..31) inside a transposed Q/dO row: bits 2 and 3
+// of q are swapped, so the eight queries one MFMA k-step takes from a lane
+// half -- 16ks + 4hl + {0..3} and 16ks + 8 + 4hl + {0..3}, the order in which
+// the S/dP accumulator holds them -- sit in eight consecutive columns and load
+// as one 16-byte read.
+__device__ __forceinline__ int qperm(int q) { return (q & ~12) | ((q & 4) << 1) | ((q & 8) >> 1); }
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void main_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const u16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
     float* __restrict__ dq_acc, float* __restrict__ dk_acc, float* __restrict__ dv_acc,
     const BwdItem* __restrict__ items, HeadMap hm, int T, int Hq, int Hkv, float c) {
-  constexpr int BKW = 128;       // keys per workgroup
-  constexpr int BQ = 32;         // query rows per step
-  constexpr int NDC = D / 8;     // 8-element chunks per row
-  constexpr int RS = D + 8;      // row-layout stride (Qs, dOs)
-  constexpr int TS = BQ + 4;     // transposed stride (Qt, dOt)
-  constexpr int KTS = BKW + 8;   // K^T stride
-  constexpr int SS = BKW + 8;    // dS stride
+  constexpr int NT = 64 * NW;     // threads
+  constexpr int BKW = 32 * NW;    // keys per workgroup, 32 per wave
+  constexpr int BQ = 32;          // query rows per step
+  constexpr int NDC = D / 8;      // 8-element chunks per row
+  constexpr int RS = D + 8;       // Qs / dOs row stride
+  constexpr int TS = BQ + 8;      // Qt / dOt row stride (row = d, permuted queries)
+  constexpr int KTS = BKW + 8;    // Kt row stride (row = d, keys)
+  constexpr int SS = BKW + 8;     // dSs row stride (row = query, keys)
+  constexpr int UNITS = 2 * 16 * NDC;          // (tensor, row pair, d chunk) staging units
+  constexpr int UPT = (UNITS + NT - 1) / NT;   // units per thread
   __shared__ __attribute__((aligned(16))) u16 Qs[BQ * RS];
   __shared__ __attribute__((aligned(16))) u16 dOs[BQ * RS];
   __shared__ __attribute__((aligned(16))) u16 Qt[D * TS];
@@ -90,6 +100,7 @@ __global__ __launch_bounds__(256, 1) void main_kernel(
   const int G = Hq / Hkv;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hl = lane >> 5, l32 = lane & 31;
+  const int l16 = lane & 15, g16 = lane >> 4;
   const size_t qrow = (size_t)Hq * D, krow = (size_t)Hkv * D;
   const int kw = it.kb + 32 * w;          // first key of this wave
   const int key = kw + l32;               // this lane's key (S/dP column)
@@ -111,25 +122,22 @@ __global__ __launch_bounds__(256, 1) void main_kernel(
       vf[kk] = b.v;
     }
   }
-  // K^T of the whole 128-key tile in LDS (B operand of dQ = dS K).
-  {
-    constexpr int NBLK = (BKW / 4) * NDC;  // (4 keys x 8 d) blocks
-    for (int blk = tid; blk < NBLK; blk += 256) {
-      const int kg = blk % (BKW / 4), dc = blk / (BKW / 4);
-      uint4 r4[4];
+  // K^T of the workgroup's keys in LDS: B operand of dQ = dS K (row = d).
+  for (int blk = tid; blk < (BKW / 4) * NDC; blk += NT) {
+    const int kg = blk % (BKW / 4), dc = blk / (BKW / 4);
+    uint4 r4[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kk = it.kb + 4 * kg + j;
-        r4[j] = kk < it.ke ? *reinterpret_cast<const uint4*>(k + (size_t)kk * krow + (size_t)g * D + dc * 8)
-                           : make_uint4(0, 0, 0, 0);
-      }
+    for (int j = 0; j < 4; ++j) {
+      const int kk = it.kb + 4 * kg + j;
+      r4[j] = kk < it.ke ? *reinterpret_cast<const uint4*>(k + (size_t)kk * krow + (size_t)g * D + dc * 8)
+                         : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint2 w2;
-        w2.x = u16_of(r4[0], e) | (u16_of(r4[1], e) << 16);
-        w2.y = u16_of(r4[2], e) | (u16_of(r4[3], e) << 16);
-        *reinterpret_cast<uint2*>(Kt + (dc * 8 + e) * KTS + 4 * kg) = w2;
-      }
+    for (int e = 0; e < 8; ++e) {
+      uint2 w2;
+      w2.x = u16_of(r4[0], e) | (u16_of(r4[1], e) << 16);
+      w2.y = u16_of(r4[2], e) | (u16_of(r4[3], e) << 16);
+      *reinterpret_cast<uint2*>(Kt + (dc * 8 + e) * KTS + 4 * kg) = w2;
     }
   }
 
@@ -137,25 +145,28 @@ __global__ __launch_bounds__(256, 1) void main_kernel(
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) { dkacc[i] = f32x16{}; dvacc[i] = f32x16{}; }
 
-  // Q / dO block staging: threads [0, 8*NDC) carry Q, [8*NDC, 16*NDC) carry dO;
-  // each holds 4 rows x 8 d.
-  const int st = tid % (8 * NDC);
-  const bool st_q = tid < 8 * NDC, st_do = tid >= 8 * NDC && tid < 16 * NDC;
-  const int st_rg = st % 8, st_dc = st / 8;
-  uint4 sreg[4];
+  // Staging of one step's Q and dO blocks: unit u = (tensor, row pair rp,
+  // d chunk dc), two rows x 8 d, row pair fastest so transposed stores of a
+  // wave land in consecutive columns.
+  uint4 sreg[UPT][2];
   float lreg = 0.f, dreg = 0.f;
-
   const int nqb = (it.r1 - it.r0 + BQ - 1) / BQ;
   const int nsteps = nqb * G;
-  auto load_step = [&](int s) {
-    const int qb = it.r0 + (s / G) * BQ, h = g * G + (s % G);
-    if (st_q || st_do) {
-      const u16* base = (st_q ? q : dO) + (size_t)h * D + st_dc * 8;
+
+  auto load_step = [&](int st) {
+    const int qb = it.r0 + (st / G) * BQ, h = g * G + (st % G);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = qb + 4 * st_rg + j;
-        sreg[j] = row < it.r1 ? *reinterpret_cast<const uint4*>(base + (size_t)row * qrow)
-                              : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < UPT; ++j) {
+      const int u = tid + NT * j;
+      if (u < UNITS) {
+        const int tsr = u / (16 * NDC), rem = u % (16 * NDC), rp = rem % 16, dc = rem / 16;
+        const u16* base = (tsr == 0 ? q : dO) + (size_t)h * D + dc * 8;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int row = qb + 2 * rp + i;
+          sreg[j][i] = row < it.r1 ? *reinterpret_cast<const uint4*>(base + (size_t)row * qrow)
+                                   : make_uint4(0, 0, 0, 0);
+        }
       }
     }
     if (tid < BQ) {
@@ -166,118 +177,148 @@ __global__ __launch_bounds__(256, 1) void main_kernel(
     }
   };
   auto store_step = [&]() {
-    if (st_q || st_do) {
-      u16* rowl = st_q ? Qs : dOs;
-      u16* trl = st_q ? Qt : dOt;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<uint4*>(rowl + (4 * st_rg + j) * RS + st_dc * 8) = sreg[j];
+    for (int j = 0; j < UPT; ++j) {
+      const int u = tid + NT * j;
+      if (u < UNITS) {
+        const int tsr = u / (16 * NDC), rem = u % (16 * NDC), rp = rem % 16, dc = rem / 16;
+        u16* rowl = tsr == 0 ? Qs : dOs;
+        u16* trl = tsr == 0 ? Qt : dOt;
+        *reinterpret_cast<uint4*>(rowl + (2 * rp) * RS + dc * 8) = sreg[j][0];
+        *reinterpret_cast<uint4*>(rowl + (2 * rp + 1) * RS + dc * 8) = sreg[j][1];
+        const int col = qperm(2 * rp);  // 2rp and 2rp+1 stay adjacent
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint2 w2;
-        w2.x = u16_of(sreg[0], e) | (u16_of(sreg[1], e) << 16);
-        w2.y = u16_of(sreg[2], e) | (u16_of(sreg[3], e) << 16);
-        *reinterpret_cast<uint2*>(trl + (st_dc * 8 + e) * TS + 4 * st_rg) = w2;
+        for (int e = 0; e < 8; ++e)
+          *reinterpret_cast<uint32_t*>(trl + (dc * 8 + e) * TS + col) =
+              u16_of(sreg[j][0], e) | (u16_of(sreg[j][1], e) << 16);
       }
     }
     if (tid < BQ) { lse2s[tid] = lreg; dels[tid] = dreg; }
   };
 
   if (nsteps > 0) load_step(0);
-  for (int s = 0; s < nsteps; ++s) {
-    const int qb = it.r0 + (s / G) * BQ, h = g * G + (s % G);
-    __syncthreads();   // previous step finished with Qs/dOs/Qt/dOt/dSs
+  for (int st = 0; st < nsteps; ++st) {
+    const int qb = it.r0 + (st / G) * BQ, h = g * G + (st % G);
+    __syncthreads();   // previous step finished with the staged blocks and dSs
     store_step();
     __syncthreads();
-    if (s + 1 < nsteps) load_step(s + 1);
+    if (st + 1 < nsteps) load_step(st + 1);
 
-    const bool wave_work = wave_keys && kw <= qb + BQ - 1;
-    if (wave_work) {
-      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+    u16* sp = dSs + 32 * w + l32;
+    if (wave_keys && kw <= qb + BQ - 1) {
       const u16* qp = Qs + l32 * RS + 8 * hl;
       const u16* op = dOs + l32 * RS + 8 * hl;
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        sacc = mfma32(lds_b128(qp + 16 * kk), kf[kk], sacc);
-        dpacc = mfma32(lds_b128(op + 16 * kk), vf[kk], dpacc);
-      }
       // element r: query row qb + 8 (r/4) + 4 hl + r%4, key column `key`
       const bool need_mask = (kw + 31 > qb) || (kw + 32 > it.ke);
-      float p[16], ds[16];
+      bf16x8 pf0, pf1, sf0, sf1;
+      {
+        f32x16 sacc = f32x16{};
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const float4 l4 = *reinterpret_cast<const float4*>(lse2s + 8 * g4 + 4 * hl);
-        const float4 d4 = *reinterpret_cast<const float4*>(dels + 8 * g4 + 4 * hl);
-        const float la[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float da[4] = {d4.x, d4.y, d4.z, d4.w};
+        for (int kk = 0; kk < D / 16; ++kk) sacc = mfma32(lds_b128(qp + 16 * kk), kf[kk], sacc);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g4 + e;
-          float x = fast_exp2(fmaf(sacc[r], c, -la[e]));
-          if (need_mask) {
-            const int row = qb + 8 * g4 + 4 * hl + e;
-            if (key > row || key >= it.ke) x = 0.f;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 l4 = *reinterpret_cast<const float4*>(lse2s + 8 * g4 + 4 * hl);
+          const float la[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g4 + e;
+            float x = fast_exp2(fmaf(sacc[r], c, -la[e]));
+            if (need_mask) {
+              const int row = qb + 8 * g4 + 4 * hl + e;
+              if (key > row || key >= it.ke) x = 0.f;
+            }
+            sacc[r] = x;
           }
-          p[r] = x;
-          ds[r] = x * (dpacc[r] - da[e]);
         }
+        pf0 = pack_bf16x8(sacc[0], sacc[1], sacc[2], sacc[3], sacc[4], sacc[5], sacc[6], sacc[7]);
+        pf1 = pack_bf16x8(sacc[8], sacc[9], sacc[10], sacc[11], sacc[12], sacc[13], sacc[14], sacc[15]);
       }
-      const bf16x8 pf0 = pack_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-      const bf16x8 pf1 = pack_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
-      const bf16x8 sf0 = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
-      const bf16x8 sf1 = pack_bf16x8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
-      // dV[key][d] += P^T dO, dK[key][d] += dS^T Q; k-slot (hl, e) is query
-      // 16 ks + 4 hl + e (e < 4) or 16 ks + 8 + 4 hl + (e - 4).
+      sched_fence();
+      {
+        // dS = P (dP - D), with P as the bf16 value the dV product consumes
+        f32x16 dpacc = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) dpacc = mfma32(lds_b128(op + 16 * kk), vf[kk], dpacc);
+        const Frag fp0{pf0}, fp1{pf1};
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 d4 = *reinterpret_cast<const float4*>(dels + 8 * g4 + 4 * hl);
+          const float da[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g4 + e;
+            const uint32_t word = r < 8 ? (r < 2 ? fp0.u.x : r < 4 ? fp0.u.y : r < 6 ? fp0.u.z : fp0.u.w)
+                                        : (r < 10 ? fp1.u.x : r < 12 ? fp1.u.y : r < 14 ? fp1.u.z : fp1.u.w);
+            const float pr = __uint_as_float((r & 1) ? (word & 0xffff0000u) : (word << 16));
+            dpacc[r] = pr * (dpacc[r] - da[e]);
+          }
+        }
+        sf0 = pack_bf16x8(dpacc[0], dpacc[1], dpacc[2], dpacc[3], dpacc[4], dpacc[5], dpacc[6], dpacc[7]);
+        sf1 = pack_bf16x8(dpacc[8], dpacc[9], dpacc[10], dpacc[11], dpacc[12], dpacc[13], dpacc[14], dpacc[15]);
+      }
+      // dV[key][d] += P^T dO and dK[key][d] += dS^T Q: B operands are one
+      // 16-byte read of the column-permuted transposed blocks.
+      sched_fence();
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const u16* ot = dOt + (32 * dt + l32) * TS + 4 * hl;
-        const u16* qt = Qt + (32 * dt + l32) * TS + 4 * hl;
-        dvacc[dt] = mfma32(pf0, lds_2xb64(ot, ot + 8), dvacc[dt]);
-        dvacc[dt] = mfma32(pf1, lds_2xb64(ot + 16, ot + 24), dvacc[dt]);
-        dkacc[dt] = mfma32(sf0, lds_2xb64(qt, qt + 8), dkacc[dt]);
-        dkacc[dt] = mfma32(sf1, lds_2xb64(qt + 16, qt + 24), dkacc[dt]);
+        const u16* ot = dOt + (32 * dt + l32) * TS + 8 * hl;
+        const u16* qt = Qt + (32 * dt + l32) * TS + 8 * hl;
+        dvacc[dt] = mfma32(pf0, lds_b128(ot), dvacc[dt]);
+        dvacc[dt] = mfma32(pf1, lds_b128(ot + 16), dvacc[dt]);
+        dkacc[dt] = mfma32(sf0, lds_b128(qt), dkacc[dt]);
+        dkacc[dt] = mfma32(sf1, lds_b128(qt + 16), dkacc[dt]);
       }
       // dS (bf16) into LDS as [query][key] for the dQ product
       const Frag f0{sf0}, f1{sf1};
-      u16* sp = dSs + 32 * w + l32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const uint32_t word = r < 8 ? (r < 2 ? f0.u.x : r < 4 ? f0.u.y : r < 6 ? f0.u.z : f0.u.w)
                                     : (r < 10 ? f1.u.x : r < 12 ? f1.u.y : r < 14 ? f1.u.z : f1.u.w);
-        const u16 val = (r & 1) ? (u16)(word >> 16) : (u16)(word & 0xffffu);
-        sp[(8 * (r >> 2) + 4 * hl + (r & 3)) * SS] = val;
+        sp[(8 * (r >> 2) + 4 * hl + (r & 3)) * SS] = (r & 1) ? (u16)(word >> 16) : (u16)(word & 0xffffu);
       }
     } else {
-      // keys of this wave are all after the block's rows: dS is zero
-      u16* sp = dSs + 32 * w + l32;
+      // this wave's keys all come after the block's rows (or past the tile): dS = 0
 #pragma unroll
       for (int r = 0; r < 16; ++r) sp[(8 * (r >> 2) + 4 * hl + (r & 3)) * SS] = 0;
     }
     __syncthreads();
-    // dQ[q][d] += dS[q][key] K[key][d]: wave w produces d columns [32 w, 32 w + 32).
-    if (32 * w < D && it.kb <= qb + BQ - 1) {
-      f32x16 acc = f32x16{};
-      const u16* ap = dSs + l32 * SS + 8 * hl;
-      const u16* bp = Kt + (32 * w + l32) * KTS + 8 * hl;
+    sched_fence();
+    // dQ[q][d] += dS[q][key] K[key][d] over all BKW keys of the workgroup, on
+    // 16x16x32 tiles; the 2 x D/16 (query, d) tiles are dealt to the waves.
+    if (it.kb <= qb + BQ - 1) {
+      const bool full_rows = qb + BQ <= it.r1;
 #pragma unroll
-      for (int ks = 0; ks < BKW / 16; ++ks) acc = mfma32(lds_b128(ap + 16 * ks), lds_b128(bp + 16 * ks), acc);
-      float* dqp = dq_acc + (size_t)h * D + 32 * w + l32;
+      for (int t = w; t < 2 * (D / 16); t += NW) {
+        const int mt = t & 1, d0 = 16 * (t >> 1);
+        const u16* bp = Kt + (d0 + l16) * KTS + 8 * g16;
+        const u16* ap = dSs + (16 * mt + l16) * SS + 8 * g16;
+        f32x4 acc = f32x4{};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = qb + 8 * (r >> 2) + 4 * hl + (r & 3);
-        if (row < it.r1) unsafeAtomicAdd(dqp + (size_t)row * qrow, acc[r]);
+        for (int ks = 0; ks < BKW / 32; ++ks)
+          acc = mfma16(lds_b128(ap + 32 * ks), lds_b128(bp + 32 * ks), acc);
+        // element r: query row qb + 16 mt + 4 g16 + r, column d0 + l16
+        float* dqp = dq_acc + (size_t)(qb + 16 * mt + 4 * g16) * qrow + (size_t)h * D + d0 + l16;
+        if (full_rows) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) unsafeAtomicAdd(dqp + (size_t)r * qrow, acc[r]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (qb + 16 * mt + 4 * g16 + r < it.r1) unsafeAtomicAdd(dqp + (size_t)r * qrow, acc[r]);
+        }
       }
     }
   }
 
   // partial dK / dV of this chunk: fp32 atomics (the cross-sequence prompt sum)
   if (wave_keys) {
+    const bool full_keys = kw + 32 <= it.ke;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kk = kw + 8 * (r >> 2) + 4 * hl + (r & 3);
-        if (kk < it.ke) {
+        if (full_keys || kk < it.ke) {
           const size_t off = (size_t)kk * krow + (size_t)g * D + 32 * dt + l32;
           unsafeAtomicAdd(dk_acc + off, dkacc[dt][r]);
           unsafeAtomicAdd(dv_acc + off, dvacc[dt][r]);
@@ -331,14 +372,14 @@ hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const voi
   // 2. main
   if ((phase_mask & 2) && n_items > 0) {
     HeadMap hm = make_headmap(n_items, pb.Hkv);
-    dim3 grid(headmap_grid(hm));
+    dim3 grid(headmap_grid(hm)), block(64 * kBwdWaves);
     const float c = pb.scale * kLog2e;
     if (pb.d == 128)
-      hipLaunchKernelGGL(main_kernel<128>, grid, dim3(256), 0, stream, (const u16*)q,
+      hipLaunchKernelGGL((main_kernel<128, kBwdWaves>), grid, block, 0, stream, (const u16*)q,
                          (const u16*)k, (const u16*)v, (const u16*)dO, lse, delta, dq_acc,
                          dk_acc, dv_acc, items_dev, hm, pb.T, pb.Hq, pb.Hkv, c);
     else
-      hipLaunchKernelGGL(main_kernel<64>, grid, dim3(256), 0, stream, (const u16*)q,
+      hipLaunchKernelGGL((main_kernel<64, kBwdWaves>), grid, block, 0, stream, (const u16*)q,
                          (const u16*)k, (const u16*)v, (const u16*)dO, lse, delta, dq_acc,
                          dk_acc, dv_acc, items_dev, hm, pb.T, pb.Hq, pb.Hkv, c);
   }

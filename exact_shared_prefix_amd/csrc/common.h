@@ -11,6 +11,7 @@ namespace dkv {
 typedef unsigned short u16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -40,6 +41,13 @@ struct FwdItem { int r0, r1, a_end, b_start; };
 // by all later rows, response keys only by their own response's later rows,
 // and the scheduler never pairs a response tile with foreign rows).
 struct BwdItem { int kb, ke, r0, r1; };
+
+// Backward workgroup shape: kBwdWaves waves of 32 keys each.
+#ifndef DKV_BWD_WAVES
+#define DKV_BWD_WAVES 8
+#endif
+constexpr int kBwdWaves = DKV_BWD_WAVES;
+constexpr int kBwdKeys = 32 * kBwdWaves;
 
 // Launch-time block -> (item, head) decomposition that keeps each head group
 // on one XCD (workgroups are dealt to the 8 XCDs round-robin by block id).
@@ -78,6 +86,12 @@ __device__ inline bool headmap_decode(const HeadMap& m, int b, int& item, int& h
 // ----------------------------------------------------------------- device --
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16x16x32: A lane -> row l%16, k = 8 (l/16) + e; B lane -> column l%16, same
+// k; D lane -> column l%16, rows 4 (l/16) + r.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 union Frag {
@@ -119,6 +133,10 @@ __device__ __forceinline__ uint32_t u16_of(const uint4& v, int e) {
   uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
 }
+
+// Compiler-only fence: memory operations are not moved across it (keeps the
+// scheduler from hoisting a later phase's LDS reads into registers early).
+__device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

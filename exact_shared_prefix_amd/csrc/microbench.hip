@@ -1,0 +1,148 @@
+// Hardware micro-benchmarks used to put the attention kernels' numbers in
+// context: sustained bf16 MFMA rate (32x32x16), and LDS read bandwidth for
+// 16-byte reads and for 8-byte transpose reads. Not part of the attention
+// path; built into a separate library (libdualkv_microbench.so).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// Four independent accumulator chains per wave so MFMA issue, not the
+// dependency latency, sets the rate. Operands come from registers.
+__global__ __launch_bounds__(256) void mfma_rate_kernel(float* out, int iters, float seed) {
+  bf16x8 a, b;
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(seed * (float)(threadIdx.x + e));
+    b[e] = (__bf16)(seed * (float)(e - (int)threadIdx.x));
+  }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int i = 0; i < iters; ++i) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+  }
+  float s = 0.f;
+  for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+// 16-byte LDS reads, conflict-free (consecutive lanes, consecutive 16 B).
+__global__ __launch_bounds__(256) void lds_b128_kernel(uint32_t* out, int iters) {
+  __shared__ __attribute__((aligned(16))) uint4 buf[4096];  // 64 KB
+  for (int i = threadIdx.x; i < 4096; i += 256) buf[i] = make_uint4(i, i + 1, i + 2, i + 3);
+  __syncthreads();
+  uint32_t acc = 0;
+  int idx = threadIdx.x;
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint4 v = buf[(idx + u * 256) & 4095];
+      acc ^= v.x + v.y + v.z + v.w;
+    }
+    idx = (idx + 64) & 4095;
+  }
+  out[blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+// 8-byte transpose reads (ds_read_b64_tr_b16) over 4-row x 16-column tiles of
+// a row-major array with a 72-dword row pitch.
+__global__ __launch_bounds__(256) void lds_tr_kernel(uint32_t* out, int iters) {
+  constexpr int PITCH = 144;  // bf16 elements per row
+  __shared__ __attribute__((aligned(16))) short buf[128 * PITCH];
+  for (int i = threadIdx.x; i < 128 * PITCH; i += 256) buf[i] = (short)i;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int j = lane & 15, g = lane >> 4;
+  uint32_t acc = 0;
+  int row0 = 4 * g + 16 * w;
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int row = (row0 + (j >> 2) + 8 * u) & 127;
+      const int col = 16 * (u & 7) + 4 * (j & 3);
+      v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16*)(buf + row * PITCH + col));
+      acc ^= (uint32_t)(v[0] + v[1] + v[2] + v[3]);
+    }
+    row0 = (row0 + 4) & 127;
+  }
+  out[blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+// Same addresses as lds_tr_kernel but plain 8-byte reads (no transpose).
+__global__ __launch_bounds__(256) void lds_b64_kernel(uint32_t* out, int iters) {
+  constexpr int PITCH = 144;
+  __shared__ __attribute__((aligned(16))) short buf[128 * PITCH];
+  for (int i = threadIdx.x; i < 128 * PITCH; i += 256) buf[i] = (short)i;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int j = lane & 15, g = lane >> 4;
+  uint32_t acc = 0;
+  int row0 = 4 * g + 16 * w;
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int row = (row0 + (j >> 2) + 8 * u) & 127;
+      const int col = 16 * (u & 7) + 4 * (j & 3);
+      const uint2 v = *reinterpret_cast<const uint2*>(buf + row * PITCH + col);
+      acc ^= v.x + v.y;
+    }
+    row0 = (row0 + 4) & 127;
+  }
+  out[blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+// Eight independent chains, 1 wave per SIMD (launch 1 block of 256 per CU).
+__global__ __launch_bounds__(256) void mfma_rate8_kernel(float* out, int iters, float seed) {
+  bf16x8 a, b;
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(seed * (float)(threadIdx.x + e));
+    b[e] = (__bf16)(seed * (float)(e - (int)threadIdx.x));
+  }
+  f32x16 c[8] = {};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) c[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[u], 0, 0, 0);
+  }
+  float s = 0.f;
+  for (int u = 0; u < 8; ++u)
+    for (int r = 0; r < 16; ++r) s += c[u][r];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+extern "C" {
+
+int dkv_mb_lds_b64(int blocks, int iters, uint32_t* out, void* stream) {
+  hipLaunchKernelGGL(lds_b64_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters);
+  return (int)hipGetLastError();
+}
+
+int dkv_mb_mfma8(int blocks, int iters, float* out, void* stream) {
+  hipLaunchKernelGGL(mfma_rate8_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters,
+                     1e-3f);
+  return (int)hipGetLastError();
+}
+
+// Each launches `blocks` workgroups of 256 threads on `stream`; returns the
+// hipError_t of the launch. FLOPs = blocks * 4 waves * iters * 4 * 32768;
+// LDS bytes = blocks * 256 * iters * 8 * (16 or 8).
+int dkv_mb_mfma(int blocks, int iters, float* out, void* stream) {
+  hipLaunchKernelGGL(mfma_rate_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters,
+                     1e-3f);
+  return (int)hipGetLastError();
+}
+
+int dkv_mb_lds_b128(int blocks, int iters, uint32_t* out, void* stream) {
+  hipLaunchKernelGGL(lds_b128_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters);
+  return (int)hipGetLastError();
+}
+
+int dkv_mb_lds_tr(int blocks, int iters, uint32_t* out, void* stream) {
+  hipLaunchKernelGGL(lds_tr_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters);
+  return (int)hipGetLastError();
+}
+
+}  // extern "C"

@@ -1,0 +1,85 @@
+"""Hardware micro-benchmarks on the current GPU (libdualkv_microbench.so).
+
+mfma_tflops(): sustained dense bf16 MFMA rate (32x32x16, register operands,
+four independent chains per wave, 8 waves per CU on every CU).
+lds_bytes_per_clk(): LDS read bandwidth per CU for 16-byte reads and for
+8-byte transpose reads, from the measured time and the GPU's clock.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdualkv_microbench.so")
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            from . import build as _build
+            _build.build()
+        _lib = ctypes.CDLL(_LIB)
+        for name in ("dkv_mb_mfma", "dkv_mb_mfma8", "dkv_mb_lds_b128", "dkv_mb_lds_b64",
+                     "dkv_mb_lds_tr"):
+            fn = getattr(_lib, name)
+            fn.restype = ctypes.c_int
+            fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    return _lib
+
+
+def _time(fn, blocks, iters, reps=3):
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream()
+    assert fn(blocks, max(1, iters // 8), out.data_ptr(), s.cuda_stream) == 0
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        assert fn(blocks, iters, out.data_ptr(), s.cuda_stream) == 0
+        e1.record(s)
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) * 1e-3)
+    return best
+
+
+def cu_count() -> int:
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def clock_hz() -> float:
+    """Peak shader clock (Hz) as the runtime reports it."""
+    props = torch.cuda.get_device_properties(0)
+    khz = getattr(props, "clock_rate", 0) or 2_400_000
+    return khz * 1e3
+
+
+def mfma_tflops(iters: int = 4096) -> float:
+    """Best of: 8 waves/CU x 4 chains, and 4 waves/CU x 8 chains."""
+    lib = _load()
+    blocks = cu_count() * 2  # 8 waves per CU
+    a = blocks * 4 * iters * 4 * 32768 / _time(lib.dkv_mb_mfma, blocks, iters) / 1e12
+    blocks = cu_count()      # 4 waves per CU
+    b = blocks * 4 * iters * 8 * 32768 / _time(lib.dkv_mb_mfma8, blocks, iters) / 1e12
+    return max(a, b)
+
+
+def lds_bytes_per_clk(iters: int = 4096) -> dict:
+    lib = _load()
+    blocks = cu_count() * 2
+    res = {}
+    for name, fn, width in (("b128", lib.dkv_mb_lds_b128, 16), ("b64", lib.dkv_mb_lds_b64, 8),
+                            ("tr_b64", lib.dkv_mb_lds_tr, 8)):
+        sec = _time(fn, blocks, iters)
+        total = blocks * 256 * iters * 8 * width
+        res[name] = total / sec / cu_count() / clock_hz()
+    return res
+
+
+if __name__ == "__main__":
+    print({"cus": cu_count(), "clock_hz": clock_hz(), "mfma_bf16_tflops": mfma_tflops(),
+           "lds_bytes_per_clk_per_cu": lds_bytes_per_clk()})
