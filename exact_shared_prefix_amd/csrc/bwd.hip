@@ -69,8 +69,24 @@ __global__ __launch_bounds__(256) void zero_kernel(float4* __restrict__ p, size_
 // as one 16-byte read.
 __device__ __forceinline__ int qperm(int q) { return (q & ~12) | ((q & 4) << 1) | ((q & 8) >> 1); }
 
+// Transposed Q/dO block in LDS: row = d, 64 column positions in 8 blocks of 8
+// (the 32 permuted queries occupy 4 of them) plus padding; the block index is
+// XOR-ed with (row >> 4) & 7. Both the transposing 4-byte stores and the
+// 16-byte MFMA operand reads then hit distinct banks.
+constexpr int kTS = 72;
+
+// MFMA operands read from LDS in blocks of this many 16-byte reads ahead of
+// the products that use them.
+#ifndef DKV_READ_AHEAD
+#define DKV_READ_AHEAD 2
+#endif
+constexpr int kReadAhead = DKV_READ_AHEAD;
+__device__ __forceinline__ int tpos(int row, int pos) {
+  return row * kTS + ((((pos >> 3) ^ (row >> 4)) & 7) << 3) + (pos & 7);
+}
+
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void main_kernel(
+__global__ __launch_bounds__(64 * NW, 1) void main_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const u16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
     float* __restrict__ dq_acc, float* __restrict__ dk_acc, float* __restrict__ dv_acc,
@@ -80,17 +96,20 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void main_kernel(
   constexpr int BQ = 32;          // query rows per step
   constexpr int NDC = D / 8;      // 8-element chunks per row
   constexpr int RS = D + 8;       // Qs / dOs row stride
-  constexpr int TS = BQ + 8;      // Qt / dOt row stride (row = d, permuted queries)
   constexpr int KTS = BKW + 8;    // Kt row stride (row = d, keys)
   constexpr int SS = BKW + 8;     // dSs row stride (row = query, keys)
-  constexpr int UNITS = 2 * 16 * NDC;          // (tensor, row pair, d chunk) staging units
+  constexpr int NDQ = 2 * (D / 16) / NW;       // dQ 16x16 tiles per wave
+  constexpr int UNITS = 2 * (BQ / 2) * NDC;    // (tensor, row pair, d chunk) staging units
   constexpr int UPT = (UNITS + NT - 1) / NT;   // units per thread
+  static_assert((2 * (D / 16)) % NW == 0 && NDQ >= 1, "dQ tiles must divide evenly over the waves");
+  static_assert(NW % 2 == 0, "dQ tiles of a wave share their query rows");
+  static_assert((D / 16) % kReadAhead == 0 && kReadAhead % 2 == 0, "read-ahead depth");
   __shared__ __attribute__((aligned(16))) u16 Qs[BQ * RS];
   __shared__ __attribute__((aligned(16))) u16 dOs[BQ * RS];
-  __shared__ __attribute__((aligned(16))) u16 Qt[D * TS];
-  __shared__ __attribute__((aligned(16))) u16 dOt[D * TS];
+  __shared__ __attribute__((aligned(16))) u16 QdOt[2][D * kTS];   // transposed [Q, dO]
   __shared__ __attribute__((aligned(16))) u16 Kt[D * KTS];
   __shared__ __attribute__((aligned(16))) u16 dSs[BQ * SS];
+  __shared__ __attribute__((aligned(16))) f32x4 dq_stash[NDQ][NT];   // dQ of the previous step
   __shared__ __attribute__((aligned(16))) float lse2s[BQ];
   __shared__ __attribute__((aligned(16))) float dels[BQ];
 
@@ -105,116 +124,141 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void main_kernel(
   const int kw = it.kb + 32 * w;          // first key of this wave
   const int key = kw + l32;               // this lane's key (S/dP column)
   const bool wave_keys = kw < it.ke;
+  const int nqb = (it.r1 - it.r0 + BQ - 1) / BQ;
+  const int nsteps = nqb * G;
 
-  // K and V fragments: B operands of S = Q K^T and dP = dO V^T
-  // (lane -> key column, 8 consecutive d).
+  // K and V fragments: B operands of S = Q K^T and dP = dO V^T (lane -> key
+  // column, 8 consecutive d). Keys past the tile end read the tile's last key:
+  // they are masked out of P and dS, and their dK/dV are never written.
   bf16x8 kf[D / 16], vf[D / 16];
   {
-    const bool ok = key < it.ke;
-    const u16* kp = k + (size_t)key * krow + (size_t)g * D + 8 * hl;
-    const u16* vp = v + (size_t)key * krow + (size_t)g * D + 8 * hl;
+    const int kc = min(key, it.ke - 1);
+    const u16* kp = k + (size_t)kc * krow + (size_t)g * D + 8 * hl;
+    const u16* vp = v + (size_t)kc * krow + (size_t)g * D + 8 * hl;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       Frag a, b;
-      a.u = ok ? *reinterpret_cast<const uint4*>(kp + 16 * kk) : make_uint4(0, 0, 0, 0);
-      b.u = ok ? *reinterpret_cast<const uint4*>(vp + 16 * kk) : make_uint4(0, 0, 0, 0);
+      a.u = *reinterpret_cast<const uint4*>(kp + 16 * kk);
+      b.u = *reinterpret_cast<const uint4*>(vp + 16 * kk);
       kf[kk] = a.v;
       vf[kk] = b.v;
     }
   }
   // K^T of the workgroup's keys in LDS: B operand of dQ = dS K (row = d).
   for (int blk = tid; blk < (BKW / 4) * NDC; blk += NT) {
-    const int kg = blk % (BKW / 4), dc = blk / (BKW / 4);
+    const int kq = blk % (BKW / 4), dc = blk / (BKW / 4);
     uint4 r4[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int kk = it.kb + 4 * kg + j;
-      r4[j] = kk < it.ke ? *reinterpret_cast<const uint4*>(k + (size_t)kk * krow + (size_t)g * D + dc * 8)
-                         : make_uint4(0, 0, 0, 0);
+      const int kk = min(it.kb + 4 * kq + j, it.ke - 1);
+      r4[j] = *reinterpret_cast<const uint4*>(k + (size_t)kk * krow + (size_t)g * D + dc * 8);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       uint2 w2;
       w2.x = u16_of(r4[0], e) | (u16_of(r4[1], e) << 16);
       w2.y = u16_of(r4[2], e) | (u16_of(r4[3], e) << 16);
-      *reinterpret_cast<uint2*>(Kt + (dc * 8 + e) * KTS + 4 * kg) = w2;
+      *reinterpret_cast<uint2*>(Kt + (dc * 8 + e) * KTS + 4 * kq) = w2;
     }
   }
+#pragma unroll
+  for (int i = 0; i < NDQ; ++i) dq_stash[i][tid] = f32x4{};
 
   f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) { dkacc[i] = f32x16{}; dvacc[i] = f32x16{}; }
 
-  // Staging of one step's Q and dO blocks: unit u = (tensor, row pair rp,
-  // d chunk dc), two rows x 8 d, row pair fastest so transposed stores of a
-  // wave land in consecutive columns.
+  // Staging of one step's Q and dO blocks through registers: unit u =
+  // (tensor, row pair rp, d chunk dc), chunk fastest. Every memory operation
+  // of the step loop is unconditional, so the compiler counts them statically
+  // and never waits for a prefetch or an atomic early: rows past the chunk
+  // end read the chunk's last row (their LSE becomes +inf when staged, which
+  // zeroes their P and dS), the last step prefetches itself, and dQ atomics of
+  // a row past the end add 0.
   uint4 sreg[UPT][2];
-  float lreg = 0.f, dreg = 0.f;
-  const int nqb = (it.r1 - it.r0 + BQ - 1) / BQ;
-  const int nsteps = nqb * G;
-
+  float lreg, dreg;
   auto load_step = [&](int st) {
     const int qb = it.r0 + (st / G) * BQ, h = g * G + (st % G);
 #pragma unroll
     for (int j = 0; j < UPT; ++j) {
-      const int u = tid + NT * j;
-      if (u < UNITS) {
-        const int tsr = u / (16 * NDC), rem = u % (16 * NDC), rp = rem % 16, dc = rem / 16;
-        const u16* base = (tsr == 0 ? q : dO) + (size_t)h * D + dc * 8;
+      const int u = (tid + NT * j) % UNITS;
+      const int tsr = u / ((BQ / 2) * NDC), rem = u % ((BQ / 2) * NDC), dc = rem % NDC, rp = rem / NDC;
+      const u16* base = (tsr == 0 ? q : dO) + (size_t)h * D + dc * 8;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int row = qb + 2 * rp + i;
-          sreg[j][i] = row < it.r1 ? *reinterpret_cast<const uint4*>(base + (size_t)row * qrow)
-                                   : make_uint4(0, 0, 0, 0);
-        }
+      for (int i = 0; i < 2; ++i) {
+        const int row = min(qb + 2 * rp + i, it.r1 - 1);
+        sreg[j][i] = *reinterpret_cast<const uint4*>(base + (size_t)row * qrow);
       }
     }
-    if (tid < BQ) {
-      const int row = qb + tid;
-      const bool ok = row < it.r1;
-      lreg = ok ? lse[(size_t)h * T + row] * kLog2e : INFINITY;
-      dreg = ok ? delta[(size_t)h * T + row] : 0.f;
-    }
+    const int row = min(qb + (lane & (BQ - 1)), it.r1 - 1);
+    lreg = lse[(size_t)h * T + row];
+    dreg = delta[(size_t)h * T + row];
   };
-  auto store_step = [&]() {
+  auto store_step = [&](int qb) {
 #pragma unroll
     for (int j = 0; j < UPT; ++j) {
       const int u = tid + NT * j;
-      if (u < UNITS) {
-        const int tsr = u / (16 * NDC), rem = u % (16 * NDC), rp = rem % 16, dc = rem / 16;
+      if (UNITS % NT == 0 || u < UNITS) {
+        const int tsr = u / ((BQ / 2) * NDC), rem = u % ((BQ / 2) * NDC), dc = rem % NDC, rp = rem / NDC;
         u16* rowl = tsr == 0 ? Qs : dOs;
-        u16* trl = tsr == 0 ? Qt : dOt;
         *reinterpret_cast<uint4*>(rowl + (2 * rp) * RS + dc * 8) = sreg[j][0];
         *reinterpret_cast<uint4*>(rowl + (2 * rp + 1) * RS + dc * 8) = sreg[j][1];
-        const int col = qperm(2 * rp);  // 2rp and 2rp+1 stay adjacent
+        u16* trl = QdOt[tsr];
+        const int col = qperm(2 * rp);  // 2rp and 2rp + 1 stay adjacent
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          *reinterpret_cast<uint32_t*>(trl + (dc * 8 + e) * TS + col) =
+          *reinterpret_cast<uint32_t*>(trl + tpos(dc * 8 + e, col)) =
               u16_of(sreg[j][0], e) | (u16_of(sreg[j][1], e) << 16);
       }
     }
-    if (tid < BQ) { lse2s[tid] = lreg; dels[tid] = dreg; }
+    if (tid < BQ) {
+      lse2s[tid] = qb + tid < it.r1 ? lreg * kLog2e : INFINITY;
+      dels[tid] = dreg;
+    }
+  };
+  // dQ atomics of the previous step, from the LDS stash (each lane its own)
+  int pend_qb = it.r0, pend_h = g * G;
+  auto issue_dq = [&]() {
+#pragma unroll
+    for (int i = 0; i < NDQ; ++i) {
+      const int t = w + NW * i;
+      const int mt = t & 1, d0 = 16 * (t >> 1);
+      const int row0 = pend_qb + 16 * mt + 4 * g16;
+      const f32x4 a4 = dq_stash[i][tid];
+      float* dqp = dq_acc + (size_t)pend_h * D + d0 + l16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = row0 + r < it.r1;
+        unsafeAtomicAdd(dqp + (size_t)min(row0 + r, it.r1 - 1) * qrow, ok ? a4[r] : 0.f);
+      }
+    }
   };
 
-  if (nsteps > 0) load_step(0);
+  load_step(0);
   for (int st = 0; st < nsteps; ++st) {
     const int qb = it.r0 + (st / G) * BQ, h = g * G + (st % G);
-    __syncthreads();   // previous step finished with the staged blocks and dSs
-    store_step();
-    __syncthreads();
-    if (st + 1 < nsteps) load_step(st + 1);
+    lds_barrier();   // previous step finished with the staged blocks and dSs
+    store_step(qb);
+    lds_barrier();
+    issue_dq();
 
     u16* sp = dSs + 32 * w + l32;
     if (wave_keys && kw <= qb + BQ - 1) {
-      const u16* qp = Qs + l32 * RS + 8 * hl;
-      const u16* op = dOs + l32 * RS + 8 * hl;
       // element r: query row qb + 8 (r/4) + 4 hl + r%4, key column `key`
       const bool need_mask = (kw + 31 > qb) || (kw + 32 > it.ke);
       bf16x8 pf0, pf1, sf0, sf1;
       {
+        const u16* qp = Qs + l32 * RS + 8 * hl;
         f32x16 sacc = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) sacc = mfma32(lds_b128(qp + 16 * kk), kf[kk], sacc);
+        for (int k0 = 0; k0 < D / 16; k0 += kReadAhead) {
+          bf16x8 xa[kReadAhead];
+#pragma unroll
+          for (int kk = 0; kk < kReadAhead; ++kk) xa[kk] = lds_b128(qp + 16 * (k0 + kk));
+#pragma unroll
+          for (int kk = 0; kk < kReadAhead; ++kk) sacc = mfma32(xa[kk], kf[k0 + kk], sacc);
+          reads_then_mfma<kReadAhead, kReadAhead>();
+        }
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const float4 l4 = *reinterpret_cast<const float4*>(lse2s + 8 * g4 + 4 * hl);
@@ -233,12 +277,19 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void main_kernel(
         pf0 = pack_bf16x8(sacc[0], sacc[1], sacc[2], sacc[3], sacc[4], sacc[5], sacc[6], sacc[7]);
         pf1 = pack_bf16x8(sacc[8], sacc[9], sacc[10], sacc[11], sacc[12], sacc[13], sacc[14], sacc[15]);
       }
-      sched_fence();
       {
         // dS = P (dP - D), with P as the bf16 value the dV product consumes
+        const u16* op = dOs + l32 * RS + 8 * hl;
         f32x16 dpacc = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) dpacc = mfma32(lds_b128(op + 16 * kk), vf[kk], dpacc);
+        for (int k0 = 0; k0 < D / 16; k0 += kReadAhead) {
+          bf16x8 xa[kReadAhead];
+#pragma unroll
+          for (int kk = 0; kk < kReadAhead; ++kk) xa[kk] = lds_b128(op + 16 * (k0 + kk));
+#pragma unroll
+          for (int kk = 0; kk < kReadAhead; ++kk) dpacc = mfma32(xa[kk], vf[k0 + kk], dpacc);
+          reads_then_mfma<kReadAhead, kReadAhead>();
+        }
         const Frag fp0{pf0}, fp1{pf1};
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
@@ -258,17 +309,39 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void main_kernel(
       }
       // dV[key][d] += P^T dO and dK[key][d] += dS^T Q: B operands are one
       // 16-byte read of the column-permuted transposed blocks.
-      sched_fence();
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        const u16* ot = dOt + (32 * dt + l32) * TS + 8 * hl;
-        const u16* qt = Qt + (32 * dt + l32) * TS + 8 * hl;
-        dvacc[dt] = mfma32(pf0, lds_b128(ot), dvacc[dt]);
-        dvacc[dt] = mfma32(pf1, lds_b128(ot + 16), dvacc[dt]);
-        dkacc[dt] = mfma32(sf0, lds_b128(qt), dkacc[dt]);
-        dkacc[dt] = mfma32(sf1, lds_b128(qt + 16), dkacc[dt]);
+      for (int d0 = 0; d0 < D / 32; d0 += kReadAhead / 2) {
+        bf16x8 tb[kReadAhead];
+#pragma unroll
+        for (int j = 0; j < kReadAhead / 2; ++j) {
+          tb[2 * j] = lds_b128(QdOt[1] + tpos(32 * (d0 + j) + l32, 8 * hl));
+          tb[2 * j + 1] = lds_b128(QdOt[1] + tpos(32 * (d0 + j) + l32, 16 + 8 * hl));
+        }
+#pragma unroll
+        for (int j = 0; j < kReadAhead / 2; ++j) {
+          dvacc[d0 + j] = mfma32(pf0, tb[2 * j], dvacc[d0 + j]);
+          dvacc[d0 + j] = mfma32(pf1, tb[2 * j + 1], dvacc[d0 + j]);
+        }
+        reads_then_mfma<kReadAhead, kReadAhead>();
       }
-      // dS (bf16) into LDS as [query][key] for the dQ product
+#pragma unroll
+      for (int d0 = 0; d0 < D / 32; d0 += kReadAhead / 2) {
+        bf16x8 tb[kReadAhead];
+#pragma unroll
+        for (int j = 0; j < kReadAhead / 2; ++j) {
+          tb[2 * j] = lds_b128(QdOt[0] + tpos(32 * (d0 + j) + l32, 8 * hl));
+          tb[2 * j + 1] = lds_b128(QdOt[0] + tpos(32 * (d0 + j) + l32, 16 + 8 * hl));
+        }
+#pragma unroll
+        for (int j = 0; j < kReadAhead / 2; ++j) {
+          dkacc[d0 + j] = mfma32(sf0, tb[2 * j], dkacc[d0 + j]);
+          dkacc[d0 + j] = mfma32(sf1, tb[2 * j + 1], dkacc[d0 + j]);
+        }
+        reads_then_mfma<kReadAhead, kReadAhead>();
+      }
+      // prefetch the next step's blocks (their registers stay live only
+      // through the dQ phase), then dS (bf16) into LDS as [query][key]
+      load_step(min(st + 1, nsteps - 1));
       const Frag f0{sf0}, f1{sf1};
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -278,51 +351,50 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void main_kernel(
       }
     } else {
       // this wave's keys all come after the block's rows (or past the tile): dS = 0
+      load_step(min(st + 1, nsteps - 1));
 #pragma unroll
       for (int r = 0; r < 16; ++r) sp[(8 * (r >> 2) + 4 * hl + (r & 3)) * SS] = 0;
     }
-    __syncthreads();
-    sched_fence();
+    lds_barrier();   // dSs complete
     // dQ[q][d] += dS[q][key] K[key][d] over all BKW keys of the workgroup, on
-    // 16x16x32 tiles; the 2 x D/16 (query, d) tiles are dealt to the waves.
-    if (it.kb <= qb + BQ - 1) {
-      const bool full_rows = qb + BQ <= it.r1;
+    // 16x16x32 tiles: the 2 x D/16 (query, d) tiles are dealt to the waves, and
+    // all tiles of a wave share their query rows (t = w + NW i keeps t & 1).
+    {
+      const u16* ap = dSs + (16 * (w & 1) + l16) * SS + 8 * g16;
+      bf16x8 da[BKW / 32];
 #pragma unroll
-      for (int t = w; t < 2 * (D / 16); t += NW) {
-        const int mt = t & 1, d0 = 16 * (t >> 1);
-        const u16* bp = Kt + (d0 + l16) * KTS + 8 * g16;
-        const u16* ap = dSs + (16 * mt + l16) * SS + 8 * g16;
-        f32x4 acc = f32x4{};
+      for (int ks = 0; ks < BKW / 32; ++ks) da[ks] = lds_b128(ap + 32 * ks);
 #pragma unroll
-        for (int ks = 0; ks < BKW / 32; ++ks)
-          acc = mfma16(lds_b128(ap + 32 * ks), lds_b128(bp + 32 * ks), acc);
-        // element r: query row qb + 16 mt + 4 g16 + r, column d0 + l16
-        float* dqp = dq_acc + (size_t)(qb + 16 * mt + 4 * g16) * qrow + (size_t)h * D + d0 + l16;
-        if (full_rows) {
+      for (int i = 0; i < NDQ; ++i) {
+        const u16* bp = Kt + (16 * ((w + NW * i) >> 1) + l16) * KTS + 8 * g16;
+        bf16x8 db[BKW / 32];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) unsafeAtomicAdd(dqp + (size_t)r * qrow, acc[r]);
-        } else {
+        for (int ks = 0; ks < BKW / 32; ++ks) db[ks] = lds_b128(bp + 32 * ks);
+        f32x4 a4 = f32x4{};
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (qb + 16 * mt + 4 * g16 + r < it.r1) unsafeAtomicAdd(dqp + (size_t)r * qrow, acc[r]);
-        }
+        for (int ks = 0; ks < BKW / 32; ++ks) a4 = mfma16(da[ks], db[ks], a4);
+        dq_stash[i][tid] = a4;
       }
     }
+    pend_qb = qb;
+    pend_h = h;
   }
+  issue_dq();
 
-  // partial dK / dV of this chunk: fp32 atomics (the cross-sequence prompt sum)
+  // partial dK / dV of this chunk: fp32 atomics (the cross-sequence prompt
+  // sum); keys past the tile end hold exact zeros and add them to the last key
   if (wave_keys) {
-    const bool full_keys = kw + 32 <= it.ke;
+    float* dkp = dk_acc + (size_t)g * D + l32;
+    float* dvp = dv_acc + (size_t)g * D + l32;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kk = kw + 8 * (r >> 2) + 4 * hl + (r & 3);
-        if (full_keys || kk < it.ke) {
-          const size_t off = (size_t)kk * krow + (size_t)g * D + 32 * dt + l32;
-          unsafeAtomicAdd(dk_acc + off, dkacc[dt][r]);
-          unsafeAtomicAdd(dv_acc + off, dvacc[dt][r]);
-        }
+        const size_t off = (size_t)min(kk, it.ke - 1) * krow + 32 * dt;
+        const bool ok = kk < it.ke;
+        unsafeAtomicAdd(dkp + off, ok ? dkacc[dt][r] : 0.f);
+        unsafeAtomicAdd(dvp + off, ok ? dvacc[dt][r] : 0.f);
       }
   }
 }

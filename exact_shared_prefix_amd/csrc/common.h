@@ -43,10 +43,7 @@ struct FwdItem { int r0, r1, a_end, b_start; };
 struct BwdItem { int kb, ke, r0, r1; };
 
 // Backward workgroup shape: kBwdWaves waves of 32 keys each.
-#ifndef DKV_BWD_WAVES
-#define DKV_BWD_WAVES 8
-#endif
-constexpr int kBwdWaves = DKV_BWD_WAVES;
+constexpr int kBwdWaves = 8;
 constexpr int kBwdKeys = 32 * kBwdWaves;
 
 // Launch-time block -> (item, head) decomposition that keeps each head group
@@ -134,9 +131,28 @@ __device__ __forceinline__ uint32_t u16_of(const uint4& v, int e) {
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
-// Compiler-only fence: memory operations are not moved across it (keeps the
-// scheduler from hoisting a later phase's LDS reads into registers early).
-__device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
+// Compiler-only fence: no instruction is scheduled across it. Used to issue a
+// block of LDS operand reads before the MFMA chain that consumes them, so the
+// reads' latency overlaps instead of each MFMA waiting on its own read.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Scheduling hint for the region that ends here: issue NR LDS reads first,
+// then NM MFMAs (so the reads' latency overlaps and each MFMA waits only for
+// its own operand).
+template <int NR, int NM>
+__device__ __forceinline__ void reads_then_mfma() {
+  __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // DS reads
+  __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);  // MFMA
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, then s_barrier; the memory clobber keeps the compiler from
+// moving memory accesses across it. Unlike __syncthreads() it does not wait
+// for outstanding global loads, direct-to-LDS loads or atomics; code that
+// needs those complete waits for them explicitly first.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

@@ -80,20 +80,21 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
     int kb, ke;
     tile_bounds(i, kb, ke);
     const u16* kbase = k + (size_t)g * D;
+    // keys past the range end read the range's last key: they are masked out
+    // of S (hence P = 0), and clamping keeps the loads unconditional so they
+    // stay in flight during the current tile's math
 #pragma unroll
     for (int j = 0; j < KLD; ++j) {
       int idx = tid + 256 * j, row = idx / NDC, ch = idx % NDC;
-      int key = kb + row;
-      kreg[j] = key < ke ? *reinterpret_cast<const uint4*>(kbase + (size_t)key * krow + ch * 8)
-                         : make_uint4(0, 0, 0, 0);
+      int key = min(kb + row, ke - 1);
+      kreg[j] = *reinterpret_cast<const uint4*>(kbase + (size_t)key * krow + ch * 8);
     }
     if (vthread) {
       const u16* vbase = v + (size_t)g * D + vdc * 8;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        int key = kb + 4 * vkg + j;
-        vreg[j] = key < ke ? *reinterpret_cast<const uint4*>(vbase + (size_t)key * krow)
-                           : make_uint4(0, 0, 0, 0);
+        int key = min(kb + 4 * vkg + j, ke - 1);
+        vreg[j] = *reinterpret_cast<const uint4*>(vbase + (size_t)key * krow);
       }
     }
   };
