@@ -19,6 +19,11 @@
 
 namespace dkv {
 
+// Column position of key j (0..63) in a V^T tile row: bits 2 and 3 of j are
+// swapped, so the eight keys one MFMA k-step takes from a lane half (16 ks +
+// 4 hl + {0..3} and 16 ks + 8 + 4 hl + {0..3}) are eight consecutive columns.
+__device__ __forceinline__ int kperm(int j) { return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1); }
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
@@ -26,7 +31,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
     HeadMap hm, int T, int Hq, int Hkv, float c /* softmax scale * log2(e) */) {
   constexpr int BK = 64;        // keys per LDS tile
   constexpr int KS = D + 8;     // K tile row stride (elements), padded against bank conflicts
-  constexpr int VS = BK + 4;    // V^T tile row stride
+  constexpr int VS = BK + 8;    // V^T tile row stride (16-byte aligned rows)
   constexpr int KLD = BK * D / 8 / 256;  // 16-byte K loads per thread per tile
   constexpr int NDC = D / 8;    // 8-element chunks per row
   __shared__ __attribute__((aligned(16))) u16 Ks[BK * KS];
@@ -80,21 +85,20 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
     int kb, ke;
     tile_bounds(i, kb, ke);
     const u16* kbase = k + (size_t)g * D;
-    // keys past the range end read the range's last key: they are masked out
-    // of S (hence P = 0), and clamping keeps the loads unconditional so they
-    // stay in flight during the current tile's math
 #pragma unroll
     for (int j = 0; j < KLD; ++j) {
       int idx = tid + 256 * j, row = idx / NDC, ch = idx % NDC;
-      int key = min(kb + row, ke - 1);
-      kreg[j] = *reinterpret_cast<const uint4*>(kbase + (size_t)key * krow + ch * 8);
+      int key = kb + row;
+      kreg[j] = key < ke ? *reinterpret_cast<const uint4*>(kbase + (size_t)key * krow + ch * 8)
+                         : make_uint4(0, 0, 0, 0);
     }
     if (vthread) {
       const u16* vbase = v + (size_t)g * D + vdc * 8;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        int key = min(kb + 4 * vkg + j, ke - 1);
-        vreg[j] = *reinterpret_cast<const uint4*>(vbase + (size_t)key * krow);
+        int key = kb + 4 * vkg + j;
+        vreg[j] = key < ke ? *reinterpret_cast<const uint4*>(vbase + (size_t)key * krow)
+                           : make_uint4(0, 0, 0, 0);
       }
     }
   };
@@ -110,7 +114,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
         uint2 w2;
         w2.x = u16_of(vreg[0], e) | (u16_of(vreg[1], e) << 16);
         w2.y = u16_of(vreg[2], e) | (u16_of(vreg[3], e) << 16);
-        *reinterpret_cast<uint2*>(Vt + (vdc * 8 + e) * VS + 4 * vkg) = w2;
+        *reinterpret_cast<uint2*>(Vt + (vdc * 8 + e) * VS + kperm(4 * vkg)) = w2;
       }
     }
   };
@@ -153,12 +157,18 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
     }
     mx = wave_swap32_max(mx);
-    const float mnew = fmaxf(m2, mx * c);
-    const float alpha = fast_exp2(m2 - mnew);
-    m2 = mnew;
-    lsum *= alpha;
+    // Lazy rescaling: the reference max m2 only moves when a row's max exceeds
+    // it by more than 8 (log2 units), so P stays below 2^8 and the O/l
+    // rescale is skipped unless some row of the wave needs it. O / l and the
+    // LSE do not depend on the reference.
+    if (__any(mx * c > m2 + 8.f)) {
+      const float mnew = fmaxf(m2, mx * c);
+      const float alpha = fast_exp2(m2 - mnew);
+      m2 = mnew;
+      lsum *= alpha;
 #pragma unroll
-    for (int i2 = 0; i2 < D / 32; ++i2) oacc[i2] *= alpha;
+      for (int i2 = 0; i2 < D / 32; ++i2) oacc[i2] *= alpha;
+    }
 
     bf16x8 pf[2][2];
     float ps = 0.f;
@@ -178,17 +188,15 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
     lsum += ps;
 
     // O^T[d][q] += V^T[d][key] P^T[key][q]; k-slot (hl, e) of both operands is
-    // key 4 hl + e (e < 4) or 8 + 4 hl + (e - 4) inside each 16-key step.
+    // key 4 hl + e (e < 4) or 8 + 4 hl + (e - 4) inside each 16-key step, which
+    // the permuted V^T columns hold as 8 consecutive elements at 8 hl.
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
-      const u16* vp = Vt + (32 * dt + l32) * VS + 4 * hl;
+      const u16* vp = Vt + (32 * dt + l32) * VS + 8 * hl;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          const u16* p0 = vp + 32 * sb + 16 * kh;
-          oacc[dt] = mfma32(lds_2xb64(p0, p0 + 8), pf[sb][kh], oacc[dt]);
-        }
+        for (int kh = 0; kh < 2; ++kh) oacc[dt] = mfma32(lds_b128(vp + 32 * sb + 16 * kh), pf[sb][kh], oacc[dt]);
     }
   }
 
