@@ -21,6 +21,20 @@ from oracle import oracle_fwd_bwd, rows_fwd_bwd, keys_dkdv, attended_keys
 from tests.conftest import to_np
 
 
+def _attended(t, P, lengths):
+    """A(t) written out independently of the oracle: a prompt row sees prompt
+    keys 0..t; a row of response n sees the whole prompt and its own response
+    up to itself."""
+    if t < P:
+        return list(range(t + 1))
+    start = P
+    for r in lengths:
+        if t < start + r:
+            return list(range(P)) + list(range(start, t + 1))
+        start += r
+    raise IndexError(t)
+
+
 def _inputs_np(inp):
     return tuple(to_np(x).astype(np.float64) for x in (inp.q, inp.k, inp.v, inp.do))
 
@@ -121,11 +135,11 @@ def test_lse_against_softmax_output_with_identity_v():
     ref = oracle_fwd_bwd(q, k, v, do, P, lengths, inp.scale, backward=False, block=3)
     for h in range(Hq):
         for t in range(T):
-            for j in attended_keys(t, P, lengths):
+            for j in _attended(t, P, lengths):
                 want = inp.scale * float(q[t, h] @ k[j, 0]) - math.log(ref["O"][t, h, j])
                 assert abs(ref["LSE"][h, t] - want) < 1e-12
             # and keys outside A(t) get exactly zero weight
-            outside = np.setdiff1d(np.arange(T), attended_keys(t, P, lengths))
+            outside = np.setdiff1d(np.arange(T), _attended(t, P, lengths))
             assert np.all(ref["O"][t, h, outside] == 0.0)
 
 
@@ -137,7 +151,7 @@ def _closed_form_scale0(v, do, P, lengths, Hq):
     LSE = np.zeros((Hq, T))
     dV = np.zeros((T, Hkv, d))
     for t in range(T):
-        A = list(attended_keys(t, P, lengths))
+        A = _attended(t, P, lengths)
         for h in range(Hq):
             g = h // G
             O[t, h] = sum(v[j, g].astype(np.float64) for j in A) / len(A)
@@ -300,6 +314,13 @@ def test_attended_keys_definition():
     assert list(attended_keys(8, P, lengths)) == [0, 1, 2, 3, 6, 7, 8]
     with pytest.raises(IndexError):
         attended_keys(9, P, lengths)
+
+
+def test_attended_keys_against_independent_definition():
+    for P, lengths in ((5, [3, 0, 4, 1]), (0, [2, 3]), (9, []), (1, [1, 1])):
+        T = P + sum(lengths)
+        for t in range(T):
+            assert list(attended_keys(t, P, lengths)) == _attended(t, P, lengths)
 
 
 def test_ragged_lengths_draw():
