@@ -196,14 +196,12 @@ def cpu_baseline(inp, budget_s: float) -> dict:
 
 
 def calibrate_copy(nbytes: int) -> None:
-    """A plain device copy of known size, for scaling HBM byte counters."""
+    """A plain copy kernel of known size (copy_kernel), for scaling the HBM
+    byte counters taken on the attention kernels."""
     import torch
-    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
-    y = torch.empty_like(x)
-    for _ in range(3):
-        y.copy_(x)
-    torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes_read": x.numel() * 4, "copy_bytes_written": y.numel() * 4}))
+    from exact_shared_prefix_amd import microbench
+    torch.cuda.set_device(0)
+    print(json.dumps(microbench.copy(nbytes)))
 
 
 def main() -> int:

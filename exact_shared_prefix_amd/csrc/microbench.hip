@@ -47,6 +47,25 @@ __global__ __launch_bounds__(256) void lds_b128_kernel(uint32_t* out, int iters)
   out[blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
+// 16-byte LDS reads with 16 independent reads in flight per lane and a 32 KB
+// buffer, so four workgroups (16 waves) fit on a CU.
+__global__ __launch_bounds__(256) void lds_b128_deep_kernel(uint32_t* out, int iters) {
+  __shared__ __attribute__((aligned(16))) uint4 buf[2048];  // 32 KB
+  for (int i = threadIdx.x; i < 2048; i += 256) buf[i] = make_uint4(i, i + 1, i + 2, i + 3);
+  __syncthreads();
+  uint32_t acc = 0;
+  int idx = threadIdx.x;
+  for (int i = 0; i < iters / 2; ++i) {
+    uint4 v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = buf[(idx + u * 128) & 2047];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) acc ^= v[u].x ^ v[u].w;
+    idx = (idx + 64) & 2047;
+  }
+  out[blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
 // 8-byte transpose reads (ds_read_b64_tr_b16) over 4-row x 16-column tiles of
 // a row-major array with a 72-dword row pitch.
 __global__ __launch_bounds__(256) void lds_tr_kernel(uint32_t* out, int iters) {
@@ -113,7 +132,22 @@ __global__ __launch_bounds__(256) void mfma_rate8_kernel(float* out, int iters, 
   out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// Plain copy of n16 16-byte words, grid-stride; each byte read once and
+// written once. Used to scale the HBM byte counters (FETCH_SIZE, WRITE_SIZE).
+__global__ __launch_bounds__(256) void copy_kernel(const uint4* __restrict__ src,
+                                                   uint4* __restrict__ dst, long n16) {
+  const long stride = (long)gridDim.x * blockDim.x;
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
 extern "C" {
+
+// Copies n16 16-byte words from src to dst (device pointers, no overlap).
+int dkv_mb_copy(const void* src, void* dst, long n16, void* stream) {
+  hipLaunchKernelGGL(copy_kernel, dim3(4096), dim3(256), 0, (hipStream_t)stream, (const uint4*)src,
+                     (uint4*)dst, n16);
+  return (int)hipGetLastError();
+}
 
 int dkv_mb_lds_b64(int blocks, int iters, uint32_t* out, void* stream) {
   hipLaunchKernelGGL(lds_b64_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters);
@@ -132,6 +166,12 @@ int dkv_mb_mfma8(int blocks, int iters, float* out, void* stream) {
 int dkv_mb_mfma(int blocks, int iters, float* out, void* stream) {
   hipLaunchKernelGGL(mfma_rate_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters,
                      1e-3f);
+  return (int)hipGetLastError();
+}
+
+// iters / 2 rounds of 16 reads: the same byte count as dkv_mb_lds_b128.
+int dkv_mb_lds_b128_deep(int blocks, int iters, uint32_t* out, void* stream) {
+  hipLaunchKernelGGL(lds_b128_deep_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters);
   return (int)hipGetLastError();
 }
 

@@ -24,10 +24,12 @@ def _load():
             _build.build()
         _lib = ctypes.CDLL(_LIB)
         for name in ("dkv_mb_mfma", "dkv_mb_mfma8", "dkv_mb_lds_b128", "dkv_mb_lds_b64",
-                     "dkv_mb_lds_tr"):
+                     "dkv_mb_lds_tr", "dkv_mb_lds_b128_deep"):
             fn = getattr(_lib, name)
             fn.restype = ctypes.c_int
             fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        _lib.dkv_mb_copy.restype = ctypes.c_int
+        _lib.dkv_mb_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p]
     return _lib
 
 
@@ -58,6 +60,27 @@ def clock_hz() -> float:
     return khz * 1e3
 
 
+def copy(nbytes: int, reps: int = 3) -> dict:
+    """Run the plain copy kernel `reps` times over nbytes (multiple of 16);
+    returns the bytes each launch reads and writes and the best GB/s."""
+    lib = _load()
+    n16 = nbytes // 16
+    src = torch.ones(n16 * 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    s = torch.cuda.current_stream()
+    best = float("inf")
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        assert lib.dkv_mb_copy(src.data_ptr(), dst.data_ptr(), n16, s.cuda_stream) == 0
+        e1.record(s)
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) * 1e-3)
+    assert torch.equal(src, dst)
+    return {"bytes_read": n16 * 16, "bytes_written": n16 * 16, "launches": reps,
+            "gbs": 2 * n16 * 16 / best / 1e9}
+
+
 def mfma_tflops(iters: int = 4096) -> float:
     """Best of: 8 waves/CU x 4 chains, and 4 waves/CU x 8 chains."""
     lib = _load()
@@ -77,6 +100,11 @@ def lds_bytes_per_clk(iters: int = 4096) -> dict:
         sec = _time(fn, blocks, iters)
         total = blocks * 256 * iters * 8 * width
         res[name] = total / sec / cu_count() / clock_hz()
+    for wg_per_cu in (2, 4):
+        blocks = cu_count() * wg_per_cu
+        sec = _time(lib.dkv_mb_lds_b128_deep, blocks, iters)
+        total = blocks * 256 * iters * 8 * 16
+        res[f"b128_deep_{4 * wg_per_cu}waves"] = total / sec / cu_count() / clock_hz()
     return res
 
 
