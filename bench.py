@@ -36,7 +36,8 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "fwd+bwd useful TFLOP/s and % bf16 MFMA peak at P=8K,R=4K,N=32"
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
-    "main_kernel": ["exact_shared_prefix_amd/csrc/bwd.hip", "exact_shared_prefix_amd/csrc/common.h"],
+    "dkv_kernel": ["exact_shared_prefix_amd/csrc/bwd.hip", "exact_shared_prefix_amd/csrc/common.h"],
+    "dq_kernel": ["exact_shared_prefix_amd/csrc/bwd.hip", "exact_shared_prefix_amd/csrc/common.h"],
     "fwd_kernel": ["exact_shared_prefix_amd/csrc/fwd.hip", "exact_shared_prefix_amd/csrc/common.h"],
 }
 
@@ -91,29 +92,23 @@ def time_steps(q, k, v, do, pk, scale, steps, warmup, phase_events=True):
     wsb = torch.empty(binding.bwd_workspace_bytes(pk, Hq, Hkv, d), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
+    phases = (binding.PHASE_PRE, binding.PHASE_MAIN, binding.PHASE_DQ, binding.PHASE_FINISH)
+
     def step(ev=None):
         if ev:
             ev[0].record(stream)
         binding.fwd(q, k, v, pk, scale, out=o, lse=lse, workspace=wsf)
+        for i, ph in enumerate(phases):
+            if ev:
+                ev[i + 1].record(stream)
+            binding.bwd(q, k, v, o, lse, do, pk, scale, dq, dk, dv, workspace=wsb, phases=ph)
         if ev:
-            ev[1].record(stream)
-        binding.bwd(q, k, v, o, lse, do, pk, scale, dq, dk, dv, workspace=wsb,
-                    phases=binding.PHASE_PRE)
-        if ev:
-            ev[2].record(stream)
-        binding.bwd(q, k, v, o, lse, do, pk, scale, dq, dk, dv, workspace=wsb,
-                    phases=binding.PHASE_MAIN)
-        if ev:
-            ev[3].record(stream)
-        binding.bwd(q, k, v, o, lse, do, pk, scale, dq, dk, dv, workspace=wsb,
-                    phases=binding.PHASE_FINISH)
-        if ev:
-            ev[4].record(stream)
+            ev[5].record(stream)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
     t_all0 = torch.cuda.Event(enable_timing=True)
     t_all1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -129,8 +124,8 @@ def time_steps(q, k, v, do, pk, scale, steps, warmup, phase_events=True):
     if phase_events:
         def avg(a, b):
             return sum(e[a].elapsed_time(e[b]) for e in evs) / steps
-        res.update(fwd_ms=avg(0, 1), bwd_pre_ms=avg(1, 2), bwd_main_ms=avg(2, 3),
-                   bwd_finish_ms=avg(3, 4), bwd_ms=avg(1, 4))
+        res.update(fwd_ms=avg(0, 1), bwd_pre_ms=avg(1, 2), bwd_dkv_ms=avg(2, 3),
+                   bwd_dq_ms=avg(3, 4), bwd_finish_ms=avg(4, 5), bwd_ms=avg(1, 5))
     del o, lse, dq, dk, dv, wsf, wsb
     return res
 
@@ -255,11 +250,14 @@ def main() -> int:
     ms = packed["ms_per_step"]
     value = flops["total"] / (ms * 1e-3) / 1e12
     log(f"[bench] packed: {ms:.2f} ms/step, {value:.1f} useful TFLOP/s "
-        f"(fwd {packed['fwd_ms']:.2f} ms, bwd {packed['bwd_ms']:.2f} ms, main {packed['bwd_main_ms']:.2f} ms)")
+        f"(fwd {packed['fwd_ms']:.2f} ms, bwd {packed['bwd_ms']:.2f} ms: dK/dV {packed['bwd_dkv_ms']:.2f} ms, "
+        f"dQ {packed['bwd_dq_ms']:.2f} ms)")
 
+    kflops = metrics.kernel_flops(P, L, inp.Hq, inp.d)
     kernels = {
-        "fwd_kernel": {"ms": packed["fwd_ms"], "flops": flops["fwd"]},
-        "main_kernel": {"ms": packed["bwd_main_ms"], "flops": flops["bwd"]},
+        "fwd_kernel": {"ms": packed["fwd_ms"], "flops": kflops["fwd_kernel"]},
+        "dkv_kernel": {"ms": packed["bwd_dkv_ms"], "flops": kflops["dkv_kernel"]},
+        "dq_kernel": {"ms": packed["bwd_dq_ms"], "flops": kflops["dq_kernel"]},
     }
     dom = max(kernels, key=lambda n: kernels[n]["ms"])
     ach = kernels[dom]["flops"] / (kernels[dom]["ms"] * 1e-3) / 1e12

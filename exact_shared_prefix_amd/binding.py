@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libdualkv.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 EXPORTS = ("dualkv_fwd_workspace_bytes", "dualkv_bwd_workspace_bytes", "dualkv_fwd",
            "dualkv_bwd", "dualkv_bwd_phases", "dualkv_status_string")
-PHASE_PRE, PHASE_MAIN, PHASE_FINISH, PHASE_ALL = 1, 2, 4, 7
+PHASE_PRE, PHASE_MAIN, PHASE_FINISH, PHASE_DQ, PHASE_ALL = 1, 2, 4, 8, 15
 
 _lib = None
 
@@ -173,8 +173,9 @@ def bwd(q, k, v, o, lse, do, pk: Packing, scale: Optional[float] = None,
     """dualkv_bwd -> (dq, dk, dv), bf16, same layouts as q, k, v.
 
     phases selects a subset of the backward's stream-ordered phases
-    (dualkv_bwd_phases); the outputs are complete only once all three ran, in
-    order, on the same workspace."""
+    (dualkv_bwd_phases: PHASE_PRE, PHASE_MAIN (dK, dV), PHASE_DQ, PHASE_FINISH);
+    the outputs are complete only once all of them ran on the same workspace,
+    PHASE_PRE first and PHASE_MAIN before PHASE_FINISH."""
     T, Hq, d = q.shape
     Hkv = k.shape[1]
     dev = q.device

@@ -19,9 +19,9 @@ hipError_t launch_fwd(const Problem& pb, const void* q, const void* k, const voi
                       float* lse, const FwdItem* items_dev, int n_items, hipStream_t stream);
 hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dO, void* dQ, void* dK,
-                      void* dV, const BwdItem* items_dev, int n_items, float* delta,
-                      float* dq_acc, float* dk_acc, float* dv_acc, hipStream_t stream,
-                      int phase_mask);
+                      void* dV, const BwdItem* items_dev, int n_items, const FwdItem* qitems_dev,
+                      int n_qitems, float* delta, float* dk_acc, float* dv_acc,
+                      hipStream_t stream, int phase_mask);
 }  // namespace dkv
 
 using namespace dkv;
@@ -118,17 +118,17 @@ hipError_t upload(void* dst, const void* src, size_t n, hipStream_t stream) {
   return staging->upload(dst, src, n, stream);
 }
 
-// Forward work list: 128-row query tiles that never straddle a segment,
-// longest (most keys) first so the tail of the grid is short.
-std::vector<FwdItem> fwd_items(const Problem& pb) {
+// Forward (and dQ) work list: query tiles of `rows` rows that never straddle
+// a segment, longest (most keys) first so the tail of the grid is short.
+std::vector<FwdItem> fwd_items(const Problem& pb, int rows = kFwdRows) {
   std::vector<FwdItem> items;
-  for (int r = 0; r < pb.P; r += kFwdRows) {
-    const int r1 = std::min(pb.P, r + kFwdRows);
+  for (int r = 0; r < pb.P; r += rows) {
+    const int r1 = std::min(pb.P, r + rows);
     items.push_back({r, r1, r1, r1});
   }
   for (int n = 0; n < pb.N; ++n) {
     const int a = pb.seg_start(n), b = pb.seg_start(n + 1);
-    for (int r = a; r < b; r += kFwdRows) items.push_back({r, std::min(b, r + kFwdRows), pb.P, a});
+    for (int r = a; r < b; r += rows) items.push_back({r, std::min(b, r + rows), pb.P, a});
   }
   std::stable_sort(items.begin(), items.end(), [](const FwdItem& x, const FwdItem& y) {
     return (x.a_end + x.r1 - x.b_start) > (y.a_end + y.r1 - y.b_start);
@@ -136,7 +136,7 @@ std::vector<FwdItem> fwd_items(const Problem& pb) {
   return items;
 }
 
-// Backward work list: 128-key tiles, each paired with the rows that attend it
+// dK/dV work list: kBwdKeys-key tiles, each paired with the rows that attend it
 // (all later rows for a prompt tile, the later rows of its own response for a
 // response tile), cut on a fixed grid of kBwdChunk-row chunks. Items are
 // ordered chunk-major so workgroups running together share query rows.
@@ -161,15 +161,15 @@ std::vector<BwdItem> bwd_items(const Problem& pb) {
 }
 
 struct BwdLayout {
-  size_t items, delta, dq, dk, dv, total;
+  size_t items, qitems, delta, dk, dv, total;
 };
 
-BwdLayout bwd_layout(const Problem& pb, size_t n_items) {
+BwdLayout bwd_layout(const Problem& pb, size_t n_items, size_t n_qitems) {
   BwdLayout L;
   size_t off = 0;
-  L.items = off; off = align_up(off + n_items * sizeof(BwdItem));
-  L.delta = off; off = align_up(off + (size_t)pb.Hq * pb.T * sizeof(float));
-  L.dq = off;    off = align_up(off + (size_t)pb.T * pb.Hq * pb.d * sizeof(float));
+  L.items = off;  off = align_up(off + n_items * sizeof(BwdItem));
+  L.qitems = off; off = align_up(off + n_qitems * sizeof(FwdItem));
+  L.delta = off;  off = align_up(off + (size_t)pb.Hq * pb.T * sizeof(float));
   L.dk = off;    off = align_up(off + (size_t)pb.T * pb.Hkv * pb.d * sizeof(float));
   L.dv = off;    off = align_up(off + (size_t)pb.T * pb.Hkv * pb.d * sizeof(float));
   L.total = off;
@@ -192,7 +192,8 @@ size_t dualkv_bwd_workspace_bytes(int P, int R, int N, const int32_t* offsets, i
   Problem pb;
   if (deterministic) return 0;
   if (check_shape(P, R, N, offsets, Hq, Hkv, d, pb) != DUALKV_OK) return 0;
-  return bwd_layout(pb, std::max<size_t>(1, bwd_items(pb).size())).total;
+  return bwd_layout(pb, std::max<size_t>(1, bwd_items(pb).size()),
+                    std::max<size_t>(1, fwd_items(pb, kDqRows).size())).total;
 }
 
 dualkv_status dualkv_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int P,
@@ -228,7 +229,7 @@ dualkv_status dualkv_bwd_phases(const void* q, const void* k, const void* v, con
   Problem pb;
   dualkv_status st = check_shape(P, R, N, offsets, Hq, Hkv, d, pb);
   if (st != DUALKV_OK) return st;
-  if (phase_mask < 1 || phase_mask > 7) return DUALKV_ERR_INVALID_ARG;
+  if (phase_mask < 1 || phase_mask > 15) return DUALKV_ERR_INVALID_ARG;
   if (deterministic) return DUALKV_ERR_UNSUPPORTED;
   if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return DUALKV_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
@@ -236,7 +237,8 @@ dualkv_status dualkv_bwd_phases(const void* q, const void* k, const void* v, con
     return DUALKV_ERR_INVALID_ARG;
   pb.scale = softmax_scale;
   const std::vector<BwdItem> items = bwd_items(pb);
-  const BwdLayout L = bwd_layout(pb, std::max<size_t>(1, items.size()));
+  const std::vector<FwdItem> qitems = fwd_items(pb, kDqRows);
+  const BwdLayout L = bwd_layout(pb, std::max<size_t>(1, items.size()), std::max<size_t>(1, qitems.size()));
   if (!workspace || workspace_bytes < L.total) return DUALKV_ERR_WORKSPACE;
   if (!aligned16(workspace)) return DUALKV_ERR_INVALID_ARG;
   if (pb.T == 0) return DUALKV_OK;
@@ -245,10 +247,14 @@ dualkv_status dualkv_bwd_phases(const void* q, const void* k, const void* v, con
   if ((phase_mask & 2) && !items.empty() &&
       upload(ws + L.items, items.data(), items.size() * sizeof(BwdItem), s) != hipSuccess)
     return DUALKV_ERR_HIP;
+  if ((phase_mask & 8) && !qitems.empty() &&
+      upload(ws + L.qitems, qitems.data(), qitems.size() * sizeof(FwdItem), s) != hipSuccess)
+    return DUALKV_ERR_HIP;
   if (launch_bwd(pb, q, k, v, o, lse, dO, dQ, dK, dV, reinterpret_cast<const BwdItem*>(ws + L.items),
-                 (int)items.size(), reinterpret_cast<float*>(ws + L.delta),
-                 reinterpret_cast<float*>(ws + L.dq), reinterpret_cast<float*>(ws + L.dk),
-                 reinterpret_cast<float*>(ws + L.dv), s, phase_mask) != hipSuccess)
+                 (int)items.size(), reinterpret_cast<const FwdItem*>(ws + L.qitems),
+                 (int)qitems.size(), reinterpret_cast<float*>(ws + L.delta),
+                 reinterpret_cast<float*>(ws + L.dk), reinterpret_cast<float*>(ws + L.dv), s,
+                 phase_mask) != hipSuccess)
     return DUALKV_ERR_HIP;
   return DUALKV_OK;
 }
@@ -259,7 +265,7 @@ dualkv_status dualkv_bwd(const void* q, const void* k, const void* v, const void
                          float softmax_scale, int deterministic, void* workspace,
                          size_t workspace_bytes, void* stream) {
   return dualkv_bwd_phases(q, k, v, o, lse, dO, dQ, dK, dV, P, R, N, offsets, Hq, Hkv, d,
-                           softmax_scale, deterministic, workspace, workspace_bytes, stream, 7);
+                           softmax_scale, deterministic, workspace, workspace_bytes, stream, 15);
 }
 
 const char* dualkv_status_string(dualkv_status s) {

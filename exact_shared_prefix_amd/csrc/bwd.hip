@@ -1,27 +1,30 @@
 // Backward kernels for shared-prompt attention.
 //
 // DualKV pages (p1 "Approach"): the backward walks the same two disjoint KV
-// regions as the forward and accumulates the shared prompt's key/value
-// gradients over all N sequences with fp32 atomics. Here:
-//  1. pre_kernel:  D_t = sum_d dO_t * O_t (fp32), and zero-fill of the fp32
-//                  accumulators for dQ, dK, dV.
-//  2. main_kernel: KV-stationary. A workgroup owns 128 keys of one KV head
-//                  (4 waves x 32 keys, K and V fragments in registers) and
-//                  walks a chunk of query rows in blocks of 32 rows, for each
-//                  of the G query heads of the group:
-//                    S = Q K^T, P = exp2(S c - LSE_2), dP = dO V^T,
-//                    dS = P (dP - D), dV += P^T dO, dK += dS^T Q,
-//                    dQ += dS K (fp32 atomics into the dQ accumulator).
-//                  A prompt tile's rows are every later row of the packed
-//                  batch, split into row chunks so the work spreads over the
-//                  chip; partial dK/dV of every chunk are added with fp32
-//                  atomics, which is where the N sequences' prompt gradients
-//                  meet.
-//  3. convert_kernel: fp32 accumulators -> bf16 (dQ, dK scaled by the softmax
-//                  scale here once).
-// MFMA orientation: S is computed with queries as rows, so a lane owns one key
-// column and the S/dS accumulators serve directly as the A operand of
-// dV = P^T dO and dK = dS^T Q. dS takes one trip through LDS for dQ = dS K.
+// regions as the forward, and the shared prompt's key/value gradients are
+// accumulated over all N sequences with fp32 atomics. Here:
+//  1. pre_kernel:  D_t = sum_d dO_t * O_t (fp32); zero_kernel clears the fp32
+//                  dK, dV accumulators.
+//  2. dkv_kernel:  key-stationary dK, dV. A workgroup owns 256 keys of one KV
+//                  head (8 waves x 32 keys) and walks the query rows that
+//                  attend them in 32-row steps, for each of the G query heads
+//                  of the group. A prompt tile's rows are every later row of
+//                  the packed batch, cut into row chunks that spread over the
+//                  chip; each chunk adds its partial dK, dV with fp32 atomics,
+//                  which is where the N sequences' prompt gradients meet.
+//     dq_kernel:   query-stationary dQ: a workgroup owns 256 query rows of one
+//                  head and walks their two KV regions like the forward,
+//                  recomputing S and dP; dQ is written once, without atomics
+//                  (fp32 atomics run at a fixed rate per lane on this GPU, and
+//                  a key-stationary dQ would need one per row, d and key tile).
+//  3. convert_kernel: fp32 dK, dV -> bf16 (dK scaled by the softmax scale).
+//
+// MFMA operands staged in LDS are kept "fragment-native": one operand of a
+// wave (64 lanes x 8 bf16) is 1 KB with lane l's 16 bytes at byte 16 l, so
+// every fragment read or write is one lane-linear 16-byte access. Operands
+// needed transposed (Q^T, dO^T for dV, dK; K^T for dQ) are produced by an
+// MFMA against a unit fragment, which moves a 32 x 32 block into accumulator
+// layout exactly (one nonzero product per element).
 #include "common.h"
 
 namespace dkv {
@@ -61,57 +64,112 @@ __global__ __launch_bounds__(256) void zero_kernel(float4* __restrict__ p, size_
     p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-// ------------------------------------------------------------------ main --
-// Column position of query q (0..31) inside a transposed Q/dO row: bits 2 and 3
-// of q are swapped, so the eight queries one MFMA k-step takes from a lane
-// half -- 16ks + 4hl + {0..3} and 16ks + 8 + 4hl + {0..3}, the order in which
-// the S/dP accumulator holds them -- sit in eight consecutive columns and load
-// as one 16-byte read.
-__device__ __forceinline__ int qperm(int q) { return (q & ~12) | ((q & 4) << 1) | ((q & 8) >> 1); }
+// ---------------------------------------------------------- fragments --
+constexpr int kFrag = 512;  // u16 elements per fragment
 
-// Transposed Q/dO block in LDS: row = d, 64 column positions in 8 blocks of 8
-// (the 32 permuted queries occupy 4 of them) plus padding; the block index is
-// XOR-ed with (row >> 4) & 7. Both the transposing 4-byte stores and the
-// 16-byte MFMA operand reads then hit distinct banks.
-constexpr int kTS = 72;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void glb_void;
 
-// MFMA operands read from LDS in blocks of this many 16-byte reads ahead of
-// the products that use them.
-#ifndef DKV_READ_AHEAD
-#define DKV_READ_AHEAD 2
-#endif
-constexpr int kReadAhead = DKV_READ_AHEAD;
-__device__ __forceinline__ int tpos(int row, int pos) {
-  return row * kTS + ((((pos >> 3) ^ (row >> 4)) & 7) << 3) + (pos & 7);
+// Direct global -> LDS copy of 16 (4) bytes per lane: lane l's bytes land at
+// lds_base + 16 l (4 l); lds_base is the same for the whole wave. Written as
+// inline assembly so that the compiler does not treat every later LDS read
+// as possibly overwritten by the copy (it would wait for all outstanding
+// memory operations before each one); the kernel waits for the copies itself.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, void* lds_base) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m) : "memory", "m0");
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void main_kernel(
+__device__ __forceinline__ bf16x8 frag_ld(const u16* f, int lane) { return lds_b128(f + 8 * lane); }
+__device__ __forceinline__ void frag_st(u16* f, int lane, bf16x8 v) {
+  Frag x{v};
+  *reinterpret_cast<uint4*>(f + 8 * lane) = x.u;
+}
+
+// B operand holding a single 1.0 at k-slot e_on (0..7) for lanes with on set.
+// Used as the right factor of an MFMA that copies its left operand into the
+// accumulator layout, i.e. transposes a fragment exactly.
+__device__ __forceinline__ bf16x8 unit_frag(bool on, int e_on) {
+  const uint32_t one = 0x3f80u << (16 * (e_on & 1));
+  const int wsel = e_on >> 1;
+  Frag f;
+  f.u.x = (on && wsel == 0) ? one : 0u;
+  f.u.y = (on && wsel == 1) ? one : 0u;
+  f.u.z = (on && wsel == 2) ? one : 0u;
+  f.u.w = (on && wsel == 3) ? one : 0u;
+  return f.v;
+}
+
+// k-slot e of lane half hl in a P / dS fragment (and in every operand that is
+// paired with one) stands for query row 8 (e / 4) + 4 hl + e % 4 of its
+// 16-row step: the row order of the 32x32 accumulator.
+//
+// Transpose of a 32 x 32 block X held as two A-operand fragments (k = columns
+// 0..15 and 16..31 in natural order): returns X in accumulator layout (lane ->
+// column, register r -> row 8 (r/4) + 4 hl + r%4).
+__device__ __forceinline__ f32x16 xpose_nat(bf16x8 a0, bf16x8 a1, int lane) {
+  asm volatile("" : "+v"(lane));
+  const int n = lane & 31, hl = lane >> 5;
+  const bool mine = hl == ((n >> 3) & 1);
+  f32x16 d = mfma32(a0, unit_frag(mine && (n >> 4) == 0, n & 7), f32x16{});
+  return mfma32(a1, unit_frag(mine && (n >> 4) == 1, n & 7), d);
+}
+__device__ __forceinline__ void pack2(const f32x16& x, bf16x8& f0, bf16x8& f1) {
+  f0 = pack_bf16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+  f1 = pack_bf16x8(x[8], x[9], x[10], x[11], x[12], x[13], x[14], x[15]);
+}
+
+__device__ __forceinline__ float bf16_elem(const bf16x8& f, int e) {
+  Frag x{f};
+  const uint32_t w = e < 2 ? x.u.x : e < 4 ? x.u.y : e < 6 ? x.u.z : x.u.w;
+  return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+}
+
+// Wait until at most N vector-memory operations of this wave (the direct
+// copies above included) are outstanding, then an LDS barrier.
+template <int N>
+__device__ __forceinline__ void vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// -------------------------------------------------------------------- dKV --
+// Wave w owns keys kb + 32 w .. + 31: V fragments and the dK, dV accumulators
+// in registers, K fragments in its own LDS slots. Per 32-row step (query rows
+// qb.., head h):
+//   S = Q K^T, P = exp2(S c - LSE log2 e), dP = dO V^T, dS = P (dP - D),
+//   dV += P^T dO, dK += dS^T Q.
+// S and dP are computed with queries as rows, so a lane owns one key and the
+// P / dS accumulators are directly the A operands of the dV / dK products.
+// Q and dO arrive as A-operand fragments by direct copies one step ahead; the
+// Q^T, dO^T B fragments are made per step, one d tile per wave.
+template <int D>
+__global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const u16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
-    float* __restrict__ dq_acc, float* __restrict__ dk_acc, float* __restrict__ dv_acc,
-    const BwdItem* __restrict__ items, HeadMap hm, int T, int Hq, int Hkv, float c) {
-  constexpr int NT = 64 * NW;     // threads
-  constexpr int BKW = 32 * NW;    // keys per workgroup, 32 per wave
-  constexpr int BQ = 32;          // query rows per step
-  constexpr int NDC = D / 8;      // 8-element chunks per row
-  constexpr int RS = D + 8;       // Qs / dOs row stride
-  constexpr int KTS = BKW + 8;    // Kt row stride (row = d, keys)
-  constexpr int SS = BKW + 8;     // dSs row stride (row = query, keys)
-  constexpr int NDQ = 2 * (D / 16) / NW;       // dQ 16x16 tiles per wave
-  constexpr int UNITS = 2 * (BQ / 2) * NDC;    // (tensor, row pair, d chunk) staging units
-  constexpr int UPT = (UNITS + NT - 1) / NT;   // units per thread
-  static_assert((2 * (D / 16)) % NW == 0 && NDQ >= 1, "dQ tiles must divide evenly over the waves");
-  static_assert(NW % 2 == 0, "dQ tiles of a wave share their query rows");
-  static_assert((D / 16) % kReadAhead == 0 && kReadAhead % 2 == 0, "read-ahead depth");
-  __shared__ __attribute__((aligned(16))) u16 Qs[BQ * RS];
-  __shared__ __attribute__((aligned(16))) u16 dOs[BQ * RS];
-  __shared__ __attribute__((aligned(16))) u16 QdOt[2][D * kTS];   // transposed [Q, dO]
-  __shared__ __attribute__((aligned(16))) u16 Kt[D * KTS];
-  __shared__ __attribute__((aligned(16))) u16 dSs[BQ * SS];
-  __shared__ __attribute__((aligned(16))) f32x4 dq_stash[NDQ][NT];   // dQ of the previous step
-  __shared__ __attribute__((aligned(16))) float lse2s[BQ];
-  __shared__ __attribute__((aligned(16))) float dels[BQ];
+    float* __restrict__ dk_acc, float* __restrict__ dv_acc, const BwdItem* __restrict__ items,
+    HeadMap hm, int T, int Hq, int Hkv, float c) {
+  constexpr int NW = kBwdWaves;
+  constexpr int BQ = 32;
+  constexpr int NKK = D / 16;     // A fragments per 32-row block
+  constexpr int NDT = D / 32;     // 32-wide d tiles
+  static_assert(kBwdKeys == 32 * NW, "one 32-key block per wave");
+  static_assert((2 * NKK) % NW == 0 && 2 * NDT <= NW, "copies and transposes per wave");
+  __shared__ __attribute__((aligned(16))) u16 QA0[NKK * kFrag];
+  __shared__ __attribute__((aligned(16))) u16 QA1[NKK * kFrag];
+  __shared__ __attribute__((aligned(16))) u16 OA0[NKK * kFrag];
+  __shared__ __attribute__((aligned(16))) u16 OA1[NKK * kFrag];
+  __shared__ __attribute__((aligned(16))) float LD0[NW * 64];   // per wave: LSE (32) | D (32)
+  __shared__ __attribute__((aligned(16))) float LD1[NW * 64];
+  __shared__ __attribute__((aligned(16))) u16 KF[NW * NKK * kFrag];   // K B fragments per wave
+  __shared__ __attribute__((aligned(16))) u16 QT[NDT * 2 * kFrag];    // Q^T B fragments [dt][ks]
+  __shared__ __attribute__((aligned(16))) u16 OT[NDT * 2 * kFrag];    // dO^T B fragments
 
   int item_id, g;
   if (!headmap_decode(hm, blockIdx.x, item_id, g)) return;
@@ -119,282 +177,320 @@ __global__ __launch_bounds__(64 * NW, 1) void main_kernel(
   const int G = Hq / Hkv;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hl = lane >> 5, l32 = lane & 31;
-  const int l16 = lane & 15, g16 = lane >> 4;
   const size_t qrow = (size_t)Hq * D, krow = (size_t)Hkv * D;
-  const int kw = it.kb + 32 * w;          // first key of this wave
-  const int key = kw + l32;               // this lane's key (S/dP column)
-  const bool wave_keys = kw < it.ke;
-  const int nqb = (it.r1 - it.r0 + BQ - 1) / BQ;
-  const int nsteps = nqb * G;
+  const int kw = it.kb + 32 * w;   // first key of this wave
+  const int key = kw + l32;        // this lane's key (S / dP column)
+  const int nsteps = ((it.r1 - it.r0 + BQ - 1) / BQ) * G;
 
-  // K and V fragments: B operands of S = Q K^T and dP = dO V^T (lane -> key
-  // column, 8 consecutive d). Keys past the tile end read the tile's last key:
-  // they are masked out of P and dS, and their dK/dV are never written.
-  bf16x8 kf[D / 16], vf[D / 16];
+  // K, V fragments (lane -> key, 8 consecutive d); keys past the tile end
+  // read the tile's last key and are masked out of P
+  u16* kfl = KF + w * NKK * kFrag;
+  bf16x8 vf[NKK];
   {
     const int kc = min(key, it.ke - 1);
     const u16* kp = k + (size_t)kc * krow + (size_t)g * D + 8 * hl;
     const u16* vp = v + (size_t)kc * krow + (size_t)g * D + 8 * hl;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      Frag a, b;
-      a.u = *reinterpret_cast<const uint4*>(kp + 16 * kk);
+    for (int kk = 0; kk < NKK; ++kk) {
+      Frag b;
       b.u = *reinterpret_cast<const uint4*>(vp + 16 * kk);
-      kf[kk] = a.v;
       vf[kk] = b.v;
+      dma16(kp + 16 * kk, kfl + kk * kFrag);
     }
   }
-  // K^T of the workgroup's keys in LDS: B operand of dQ = dS K (row = d).
-  for (int blk = tid; blk < (BKW / 4) * NDC; blk += NT) {
-    const int kq = blk % (BKW / 4), dc = blk / (BKW / 4);
-    uint4 r4[4];
+  // complete the V loads here, so that no wait for them lands inside the step
+  // loop (where it would also wait for the copies in flight)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int kk = min(it.kb + 4 * kq + j, it.ke - 1);
-      r4[j] = *reinterpret_cast<const uint4*>(k + (size_t)kk * krow + (size_t)g * D + dc * 8);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint2 w2;
-      w2.x = u16_of(r4[0], e) | (u16_of(r4[1], e) << 16);
-      w2.y = u16_of(r4[2], e) | (u16_of(r4[3], e) << 16);
-      *reinterpret_cast<uint2*>(Kt + (dc * 8 + e) * KTS + 4 * kq) = w2;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < NDQ; ++i) dq_stash[i][tid] = f32x4{};
+  for (int kk = 0; kk < NKK; ++kk) asm volatile("" ::"v"(vf[kk]));
 
-  f32x16 dkacc[D / 32], dvacc[D / 32];
+  f32x16 dkacc[NDT], dvacc[NDT];
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) { dkacc[i] = f32x16{}; dvacc[i] = f32x16{}; }
+  for (int dt = 0; dt < NDT; ++dt) { dkacc[dt] = f32x16{}; dvacc[dt] = f32x16{}; }
 
-  // Staging of one step's Q and dO blocks through registers: unit u =
-  // (tensor, row pair rp, d chunk dc), chunk fastest. Every memory operation
-  // of the step loop is unconditional, so the compiler counts them statically
-  // and never waits for a prefetch or an atomic early: rows past the chunk
-  // end read the chunk's last row (their LSE becomes +inf when staged, which
-  // zeroes their P and dS), the last step prefetches itself, and dQ atomics of
-  // a row past the end add 0.
-  uint4 sreg[UPT][2];
-  float lreg, dreg;
-  auto load_step = [&](int st) {
-    const int qb = it.r0 + (st / G) * BQ, h = g * G + (st % G);
+  // Copies for step st: fragments f = w, w + NW, ... of [Q | dO], and this
+  // wave's own copy of the 32 LSE and D values. Rows past the chunk end read
+  // its last row; their P is masked to zero.
+  auto stage = [&](int st, u16* qa, u16* oa, float* ld) {
+    const int qb = it.r0 + (st / G) * BQ, h = g * G + st % G;
+    const int row = min(qb + l32, it.r1 - 1);
+    const u16* qp = q + (size_t)row * qrow + (size_t)h * D + 8 * hl;
+    const u16* op = dO + (size_t)row * qrow + (size_t)h * D + 8 * hl;
 #pragma unroll
-    for (int j = 0; j < UPT; ++j) {
-      const int u = (tid + NT * j) % UNITS;
-      const int tsr = u / ((BQ / 2) * NDC), rem = u % ((BQ / 2) * NDC), dc = rem % NDC, rp = rem / NDC;
-      const u16* base = (tsr == 0 ? q : dO) + (size_t)h * D + dc * 8;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int row = min(qb + 2 * rp + i, it.r1 - 1);
-        sreg[j][i] = *reinterpret_cast<const uint4*>(base + (size_t)row * qrow);
-      }
+    for (int j = 0; j < 2 * NKK / NW; ++j) {
+      const int f = w + NW * j;
+      if (f < NKK) dma16(qp + 16 * f, qa + f * kFrag);
+      else dma16(op + 16 * (f - NKK), oa + (f - NKK) * kFrag);
     }
-    const int row = min(qb + (lane & (BQ - 1)), it.r1 - 1);
-    lreg = lse[(size_t)h * T + row];
-    dreg = delta[(size_t)h * T + row];
-  };
-  auto store_step = [&](int qb) {
-#pragma unroll
-    for (int j = 0; j < UPT; ++j) {
-      const int u = tid + NT * j;
-      if (UNITS % NT == 0 || u < UNITS) {
-        const int tsr = u / ((BQ / 2) * NDC), rem = u % ((BQ / 2) * NDC), dc = rem % NDC, rp = rem / NDC;
-        u16* rowl = tsr == 0 ? Qs : dOs;
-        *reinterpret_cast<uint4*>(rowl + (2 * rp) * RS + dc * 8) = sreg[j][0];
-        *reinterpret_cast<uint4*>(rowl + (2 * rp + 1) * RS + dc * 8) = sreg[j][1];
-        u16* trl = QdOt[tsr];
-        const int col = qperm(2 * rp);  // 2rp and 2rp + 1 stay adjacent
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          *reinterpret_cast<uint32_t*>(trl + tpos(dc * 8 + e, col)) =
-              u16_of(sreg[j][0], e) | (u16_of(sreg[j][1], e) << 16);
-      }
-    }
-    if (tid < BQ) {
-      lse2s[tid] = qb + tid < it.r1 ? lreg * kLog2e : INFINITY;
-      dels[tid] = dreg;
-    }
-  };
-  // dQ atomics of the previous step, from the LDS stash (each lane its own)
-  int pend_qb = it.r0, pend_h = g * G;
-  auto issue_dq = [&]() {
-#pragma unroll
-    for (int i = 0; i < NDQ; ++i) {
-      const int t = w + NW * i;
-      const int mt = t & 1, d0 = 16 * (t >> 1);
-      const int row0 = pend_qb + 16 * mt + 4 * g16;
-      const f32x4 a4 = dq_stash[i][tid];
-      float* dqp = dq_acc + (size_t)pend_h * D + d0 + l16;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool ok = row0 + r < it.r1;
-        unsafeAtomicAdd(dqp + (size_t)min(row0 + r, it.r1 - 1) * qrow, ok ? a4[r] : 0.f);
-      }
-    }
+    dma4((hl ? delta : lse) + (size_t)h * T + row, ld + 64 * w);
   };
 
-  load_step(0);
-  for (int st = 0; st < nsteps; ++st) {
-    const int qb = it.r0 + (st / G) * BQ, h = g * G + (st % G);
-    lds_barrier();   // previous step finished with the staged blocks and dSs
-    store_step(qb);
-    lds_barrier();
-    issue_dq();
+  auto step = [&](int st, const u16* qa, const u16* oa, const float* ld, u16* qan, u16* oan,
+                  float* ldn) {
+    const int qb = it.r0 + (st / G) * BQ;
+    vm_barrier<0>();   // this step's copies landed; every wave is done with the last step
+    if (st + 1 < nsteps) stage(st + 1, qan, oan, ldn);
 
-    u16* sp = dSs + 32 * w + l32;
-    if (wave_keys && kw <= qb + BQ - 1) {
-      // element r: query row qb + 8 (r/4) + 4 hl + r%4, key column `key`
-      const bool need_mask = (kw + 31 > qb) || (kw + 32 > it.ke);
-      bf16x8 pf0, pf1, sf0, sf1;
-      {
-        const u16* qp = Qs + l32 * RS + 8 * hl;
-        f32x16 sacc = f32x16{};
+    // Q^T (job < NDT) and dO^T B fragments of d tile job % NDT
+    if (w < 2 * NDT) {
+      const int dt = w % NDT;
+      const u16* src = w < NDT ? qa : oa;
+      u16* dst = w < NDT ? QT : OT;
+      bf16x8 f0, f1;
+      pack2(xpose_nat(frag_ld(src + 2 * dt * kFrag, lane), frag_ld(src + (2 * dt + 1) * kFrag, lane), lane),
+            f0, f1);
+      frag_st(dst + (2 * dt) * kFrag, lane, f0);
+      frag_st(dst + (2 * dt + 1) * kFrag, lane, f1);
+    }
+
+    // accumulator register r <-> query row qb + 8 (r/4) + 4 hl + r%4
+    bf16x8 pf[2], sf[2];
+    const bool active = kw < it.ke && kw <= qb + BQ - 1;
+    if (active) {
+      f32x16 sacc = f32x16{};
 #pragma unroll
-        for (int k0 = 0; k0 < D / 16; k0 += kReadAhead) {
-          bf16x8 xa[kReadAhead];
-#pragma unroll
-          for (int kk = 0; kk < kReadAhead; ++kk) xa[kk] = lds_b128(qp + 16 * (k0 + kk));
-#pragma unroll
-          for (int kk = 0; kk < kReadAhead; ++kk) sacc = mfma32(xa[kk], kf[k0 + kk], sacc);
-          reads_then_mfma<kReadAhead, kReadAhead>();
-        }
+      for (int kk = 0; kk < NKK; ++kk)
+        sacc = mfma32(frag_ld(qa + kk * kFrag, lane), frag_ld(kfl + kk * kFrag, lane), sacc);
+      const float* lw = ld + 64 * w;
+      if ((kw + 31 > qb) || (kw + 32 > it.ke) || (qb + BQ > it.r1)) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const float4 l4 = *reinterpret_cast<const float4*>(lse2s + 8 * g4 + 4 * hl);
-          const float la[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float4 l4 = *reinterpret_cast<const float4*>(lw + 8 * g4 + 4 * hl);
+          const float la[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g4 + e;
-            float x = fast_exp2(fmaf(sacc[r], c, -la[e]));
-            if (need_mask) {
-              const int row = qb + 8 * g4 + 4 * hl + e;
-              if (key > row || key >= it.ke) x = 0.f;
-            }
-            sacc[r] = x;
+            const int row = qb + 8 * g4 + 4 * hl + e;
+            const float p = fast_exp2(fmaf(sacc[4 * g4 + e], c, -la[e]));
+            sacc[4 * g4 + e] = (key > row || key >= it.ke || row >= it.r1) ? 0.f : p;
           }
         }
-        pf0 = pack_bf16x8(sacc[0], sacc[1], sacc[2], sacc[3], sacc[4], sacc[5], sacc[6], sacc[7]);
-        pf1 = pack_bf16x8(sacc[8], sacc[9], sacc[10], sacc[11], sacc[12], sacc[13], sacc[14], sacc[15]);
-      }
-      {
-        // dS = P (dP - D), with P as the bf16 value the dV product consumes
-        const u16* op = dOs + l32 * RS + 8 * hl;
-        f32x16 dpacc = f32x16{};
-#pragma unroll
-        for (int k0 = 0; k0 < D / 16; k0 += kReadAhead) {
-          bf16x8 xa[kReadAhead];
-#pragma unroll
-          for (int kk = 0; kk < kReadAhead; ++kk) xa[kk] = lds_b128(op + 16 * (k0 + kk));
-#pragma unroll
-          for (int kk = 0; kk < kReadAhead; ++kk) dpacc = mfma32(xa[kk], vf[k0 + kk], dpacc);
-          reads_then_mfma<kReadAhead, kReadAhead>();
-        }
-        const Frag fp0{pf0}, fp1{pf1};
+      } else {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const float4 d4 = *reinterpret_cast<const float4*>(dels + 8 * g4 + 4 * hl);
-          const float da[4] = {d4.x, d4.y, d4.z, d4.w};
+          const float4 l4 = *reinterpret_cast<const float4*>(lw + 8 * g4 + 4 * hl);
+          const float la[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g4 + e;
-            const uint32_t word = r < 8 ? (r < 2 ? fp0.u.x : r < 4 ? fp0.u.y : r < 6 ? fp0.u.z : fp0.u.w)
-                                        : (r < 10 ? fp1.u.x : r < 12 ? fp1.u.y : r < 14 ? fp1.u.z : fp1.u.w);
-            const float pr = __uint_as_float((r & 1) ? (word & 0xffff0000u) : (word << 16));
-            dpacc[r] = pr * (dpacc[r] - da[e]);
-          }
+          for (int e = 0; e < 4; ++e) sacc[4 * g4 + e] = fast_exp2(fmaf(sacc[4 * g4 + e], c, -la[e]));
         }
-        sf0 = pack_bf16x8(dpacc[0], dpacc[1], dpacc[2], dpacc[3], dpacc[4], dpacc[5], dpacc[6], dpacc[7]);
-        sf1 = pack_bf16x8(dpacc[8], dpacc[9], dpacc[10], dpacc[11], dpacc[12], dpacc[13], dpacc[14], dpacc[15]);
       }
-      // dV[key][d] += P^T dO and dK[key][d] += dS^T Q: B operands are one
-      // 16-byte read of the column-permuted transposed blocks.
-#pragma unroll
-      for (int d0 = 0; d0 < D / 32; d0 += kReadAhead / 2) {
-        bf16x8 tb[kReadAhead];
-#pragma unroll
-        for (int j = 0; j < kReadAhead / 2; ++j) {
-          tb[2 * j] = lds_b128(QdOt[1] + tpos(32 * (d0 + j) + l32, 8 * hl));
-          tb[2 * j + 1] = lds_b128(QdOt[1] + tpos(32 * (d0 + j) + l32, 16 + 8 * hl));
-        }
-#pragma unroll
-        for (int j = 0; j < kReadAhead / 2; ++j) {
-          dvacc[d0 + j] = mfma32(pf0, tb[2 * j], dvacc[d0 + j]);
-          dvacc[d0 + j] = mfma32(pf1, tb[2 * j + 1], dvacc[d0 + j]);
-        }
-        reads_then_mfma<kReadAhead, kReadAhead>();
-      }
-#pragma unroll
-      for (int d0 = 0; d0 < D / 32; d0 += kReadAhead / 2) {
-        bf16x8 tb[kReadAhead];
-#pragma unroll
-        for (int j = 0; j < kReadAhead / 2; ++j) {
-          tb[2 * j] = lds_b128(QdOt[0] + tpos(32 * (d0 + j) + l32, 8 * hl));
-          tb[2 * j + 1] = lds_b128(QdOt[0] + tpos(32 * (d0 + j) + l32, 16 + 8 * hl));
-        }
-#pragma unroll
-        for (int j = 0; j < kReadAhead / 2; ++j) {
-          dkacc[d0 + j] = mfma32(sf0, tb[2 * j], dkacc[d0 + j]);
-          dkacc[d0 + j] = mfma32(sf1, tb[2 * j + 1], dkacc[d0 + j]);
-        }
-        reads_then_mfma<kReadAhead, kReadAhead>();
-      }
-      // prefetch the next step's blocks (their registers stay live only
-      // through the dQ phase), then dS (bf16) into LDS as [query][key]
-      load_step(min(st + 1, nsteps - 1));
-      const Frag f0{sf0}, f1{sf1};
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint32_t word = r < 8 ? (r < 2 ? f0.u.x : r < 4 ? f0.u.y : r < 6 ? f0.u.z : f0.u.w)
-                                    : (r < 10 ? f1.u.x : r < 12 ? f1.u.y : r < 14 ? f1.u.z : f1.u.w);
-        sp[(8 * (r >> 2) + 4 * hl + (r & 3)) * SS] = (r & 1) ? (u16)(word >> 16) : (u16)(word & 0xffffu);
-      }
-    } else {
-      // this wave's keys all come after the block's rows (or past the tile): dS = 0
-      load_step(min(st + 1, nsteps - 1));
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sp[(8 * (r >> 2) + 4 * hl + (r & 3)) * SS] = 0;
-    }
-    lds_barrier();   // dSs complete
-    // dQ[q][d] += dS[q][key] K[key][d] over all BKW keys of the workgroup, on
-    // 16x16x32 tiles: the 2 x D/16 (query, d) tiles are dealt to the waves, and
-    // all tiles of a wave share their query rows (t = w + NW i keeps t & 1).
-    {
-      const u16* ap = dSs + (16 * (w & 1) + l16) * SS + 8 * g16;
-      bf16x8 da[BKW / 32];
-#pragma unroll
-      for (int ks = 0; ks < BKW / 32; ++ks) da[ks] = lds_b128(ap + 32 * ks);
-#pragma unroll
-      for (int i = 0; i < NDQ; ++i) {
-        const u16* bp = Kt + (16 * ((w + NW * i) >> 1) + l16) * KTS + 8 * g16;
-        bf16x8 db[BKW / 32];
-#pragma unroll
-        for (int ks = 0; ks < BKW / 32; ++ks) db[ks] = lds_b128(bp + 32 * ks);
-        f32x4 a4 = f32x4{};
-#pragma unroll
-        for (int ks = 0; ks < BKW / 32; ++ks) a4 = mfma16(da[ks], db[ks], a4);
-        dq_stash[i][tid] = a4;
-      }
-    }
-    pend_qb = qb;
-    pend_h = h;
-  }
-  issue_dq();
+      pack2(sacc, pf[0], pf[1]);
 
-  // partial dK / dV of this chunk: fp32 atomics (the cross-sequence prompt
-  // sum); keys past the tile end hold exact zeros and add them to the last key
-  if (wave_keys) {
-    float* dkp = dk_acc + (size_t)g * D + l32;
-    float* dvp = dv_acc + (size_t)g * D + l32;
+      f32x16 dpacc = f32x16{};
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+      for (int kk = 0; kk < NKK; ++kk) dpacc = mfma32(frag_ld(oa + kk * kFrag, lane), vf[kk], dpacc);
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const float4 d4 = *reinterpret_cast<const float4*>(lw + 32 + 8 * g4 + 4 * hl);
+        const float da[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g4 + e;
+          // dS from the bf16 P that the dV product uses
+          dpacc[r] = bf16_elem(pf[r >> 3], r & 7) * (dpacc[r] - da[e]);
+        }
+      }
+      pack2(dpacc, sf[0], sf[1]);
+    }
+    lds_barrier();   // Q^T, dO^T fragments complete
+
+    if (active) {
+      // dV[key][d] += P^T dO, dK[key][d] += dS^T Q
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) dvacc[dt] = mfma32(pf[ks], frag_ld(OT + (2 * dt + ks) * kFrag, lane), dvacc[dt]);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) dkacc[dt] = mfma32(sf[ks], frag_ld(QT + (2 * dt + ks) * kFrag, lane), dkacc[dt]);
+    }
+  };
+
+  // The step loop alternates between two statically distinct buffer sets.
+  if (nsteps > 0) stage(0, QA0, OA0, LD0);
+  for (int st = 0; st < nsteps; st += 2) {
+    step(st, QA0, OA0, LD0, QA1, OA1, LD1);
+    if (st + 1 < nsteps) step(st + 1, QA1, OA1, LD1, QA0, OA0, LD0);
+  }
+
+  // partial dK / dV of this chunk (where the N sequences' prompt gradients
+  // meet); keys past the tile end add exact zeros to the tile's last key
+  if (kw < it.ke) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      float* dkp = dk_acc + (size_t)g * D + 32 * dt + l32;
+      float* dvp = dv_acc + (size_t)g * D + 32 * dt + l32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kk = kw + 8 * (r >> 2) + 4 * hl + (r & 3);
-        const size_t off = (size_t)min(kk, it.ke - 1) * krow + 32 * dt;
+        const size_t off = (size_t)min(kk, it.ke - 1) * krow;
         const bool ok = kk < it.ke;
         unsafeAtomicAdd(dkp + off, ok ? dkacc[dt][r] : 0.f);
         unsafeAtomicAdd(dvp + off, ok ? dvacc[dt][r] : 0.f);
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------- dQ --
+// Query-stationary dQ. A workgroup (8 waves x 32 rows) owns 256 query rows of
+// one head inside one segment and walks the same two KV regions as the
+// forward: for each 64-key tile, S^T = K Q^T, P^T = exp2(S^T c - LSE log2 e),
+// dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T. dQ stays in
+// registers and is written once, so no atomics are needed. K and V tiles
+// arrive by direct global -> LDS copies one tile ahead as A-operand fragments;
+// K^T fragments are made from them by MFMA transposes.
+
+template <int D>
+__global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
+    const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
+    const u16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
+    u16* __restrict__ dQ, const FwdItem* __restrict__ items, HeadMap hm, int T, int Hq, int Hkv,
+    float c, float scale) {
+  constexpr int NW = kDqWaves;
+  constexpr int BK = 64;          // keys per tile
+  constexpr int NKK = D / 16;
+  constexpr int NDT = D / 32;
+  constexpr int NTF = 2 * NKK;    // K (or V) fragments per tile: 2 key blocks x NKK
+  constexpr int NJOB = 2 * NTF;   // copies per tile (K and V)
+  static_assert(NJOB % NW == 0, "copies per wave");
+  __shared__ __attribute__((aligned(16))) u16 KA0[NTF * kFrag];
+  __shared__ __attribute__((aligned(16))) u16 KA1[NTF * kFrag];
+  __shared__ __attribute__((aligned(16))) u16 VA0[NTF * kFrag];
+  __shared__ __attribute__((aligned(16))) u16 VA1[NTF * kFrag];
+  __shared__ __attribute__((aligned(16))) u16 KT[2 * NDT * 2 * kFrag];   // [kb2][dt][ks]
+
+  int item_id, h;
+  if (!headmap_decode(hm, blockIdx.x, item_id, h)) return;
+  const FwdItem it = items[item_id];
+  const int G = Hq / Hkv;
+  const int g = h / G;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int hl = lane >> 5, l32 = lane & 31;
+  const int t0 = it.r0 + 32 * w;   // first query row of this wave
+  const int t = t0 + l32;          // this lane's query row
+  const int tc = min(t, it.r1 - 1);
+  const bool wave_rows = t0 < it.r1;
+  const size_t qrow = (size_t)Hq * D, krow = (size_t)Hkv * D;
+
+  // Q, dO fragments: B operands (lane -> query column, 8 consecutive d)
+  bf16x8 qf[NKK], of[NKK];
+  {
+    const u16* qp = q + (size_t)tc * qrow + (size_t)h * D + 8 * hl;
+    const u16* op = dO + (size_t)tc * qrow + (size_t)h * D + 8 * hl;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      Frag a, b;
+      a.u = *reinterpret_cast<const uint4*>(qp + 16 * kk);
+      b.u = *reinterpret_cast<const uint4*>(op + 16 * kk);
+      qf[kk] = a.v;
+      of[kk] = b.v;
+    }
+  }
+  const float lse2 = lse[(size_t)h * T + tc] * kLog2e;
+  const float dl = delta[(size_t)h * T + tc];
+  // complete these loads before the tile loop (see the forward-copy waits)
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) asm volatile("" ::"v"(qf[kk]), "v"(of[kk]));
+  asm volatile("" ::"v"(lse2), "v"(dl));
+
+  f32x16 dqacc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) dqacc[dt] = f32x16{};
+
+  const int nA = (it.a_end + BK - 1) / BK;
+  const int nB = it.r1 > it.b_start ? (it.r1 - it.b_start + BK - 1) / BK : 0;
+  const int ntiles = nA + nB;
+  auto tile_bounds = [&](int i, int& kb, int& ke) {
+    if (i < nA) { kb = i * BK; ke = it.a_end; }
+    else { kb = it.b_start + (i - nA) * BK; ke = it.r1; }
+  };
+  // copies of tile i: job f = w, w + NW, ...: tensor f / NTF, key block
+  // (f / NKK) % 2, d chunk f % NKK; keys past the region end read its last key
+  auto stage = [&](int i, u16* ka, u16* va) {
+    int kb, ke;
+    tile_bounds(i, kb, ke);
+#pragma unroll
+    for (int j = 0; j < NJOB / NW; ++j) {
+      const int f = w + NW * j;
+      const int kb2 = (f / NKK) % 2, kk = f % NKK;
+      const int key = min(kb + 32 * kb2 + l32, ke - 1);
+      const u16* src = (f < NTF ? k : v) + (size_t)key * krow + (size_t)g * D + 16 * kk + 8 * hl;
+      dma16(src, (f < NTF ? ka : va) + (f % NTF) * kFrag);
+    }
+  };
+
+  auto tile = [&](int i, const u16* ka, const u16* va, u16* kan, u16* van) {
+    int kb, ke;
+    tile_bounds(i, kb, ke);
+    vm_barrier<0>();   // tile i's copies landed; every wave is done with tile i - 1
+    if (i + 1 < ntiles) stage(i + 1, kan, van);
+    // K^T A fragments (lane -> d, k-slots in accumulator key order)
+#pragma unroll
+    for (int p = w; p < 2 * NDT; p += NW) {
+      const int kb2 = p / NDT, dt = p % NDT;
+      bf16x8 f0, f1;
+      pack2(xpose_nat(frag_ld(ka + (kb2 * NKK + 2 * dt) * kFrag, lane),
+                      frag_ld(ka + (kb2 * NKK + 2 * dt + 1) * kFrag, lane), lane),
+            f0, f1);
+      frag_st(KT + ((kb2 * NDT + dt) * 2) * kFrag, lane, f0);
+      frag_st(KT + ((kb2 * NDT + dt) * 2 + 1) * kFrag, lane, f1);
+    }
+    lds_barrier();
+    if (!wave_rows) return;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      const int k0 = kb + 32 * kb2;   // first key of this 32-key block
+      if (k0 > t0 + 31 || k0 >= ke) continue;
+      // S^T[key][query]: register r <-> key k0 + 8 (r/4) + 4 hl + r%4
+      f32x16 sacc = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) sacc = mfma32(frag_ld(ka + (kb2 * NKK + kk) * kFrag, lane), qf[kk], sacc);
+      const bool need_mask = (k0 + 31 > t0) || (k0 + 32 > ke);
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          const float p = fast_exp2(fmaf(sacc[r], c, -lse2));
+          sacc[r] = (key > t || key >= ke) ? 0.f : p;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = fast_exp2(fmaf(sacc[r], c, -lse2));
+      }
+      bf16x8 pf[2];
+      pack2(sacc, pf[0], pf[1]);
+      f32x16 dpacc = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) dpacc = mfma32(frag_ld(va + (kb2 * NKK + kk) * kFrag, lane), of[kk], dpacc);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dpacc[r] = bf16_elem(pf[r >> 3], r & 7) * (dpacc[r] - dl);
+      bf16x8 sf[2];
+      pack2(dpacc, sf[0], sf[1]);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          dqacc[dt] = mfma32(frag_ld(KT + ((kb2 * NDT + dt) * 2 + ks) * kFrag, lane), sf[ks], dqacc[dt]);
+    }
+  };
+
+  if (ntiles > 0) stage(0, KA0, VA0);
+  for (int i = 0; i < ntiles; i += 2) {
+    tile(i, KA0, VA0, KA1, VA1);
+    if (i + 1 < ntiles) tile(i + 1, KA1, VA1, KA0, VA0);
+  }
+
+  // dQ = scale * dQ^T^T: lane -> query row t, register r -> d 32 dt + 8 (r/4) + 4 hl + r%4
+  if (t < it.r1) {
+    u16* dqp = dQ + (size_t)t * qrow + (size_t)h * D + 4 * hl;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        uint2 w2;
+        w2.x = pack_bf16x2(dqacc[dt][4 * g4 + 0] * scale, dqacc[dt][4 * g4 + 1] * scale);
+        w2.y = pack_bf16x2(dqacc[dt][4 * g4 + 2] * scale, dqacc[dt][4 * g4 + 3] * scale);
+        *reinterpret_cast<uint2*>(dqp + 32 * dt + 8 * g4) = w2;
       }
   }
 }
@@ -420,11 +516,12 @@ static int stream_grid(size_t n4) {
 
 hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dO, void* dQ, void* dK,
-                      void* dV, const BwdItem* items_dev, int n_items, float* delta,
-                      float* dq_acc, float* dk_acc, float* dv_acc, hipStream_t stream,
-                      int phase_mask) {
-  const size_t nq = (size_t)pb.T * pb.Hq * pb.d, nk = (size_t)pb.T * pb.Hkv * pb.d;
-  // 1. D and zeroed accumulators
+                      void* dV, const BwdItem* items_dev, int n_items, const FwdItem* qitems_dev,
+                      int n_qitems, float* delta, float* dk_acc, float* dv_acc,
+                      hipStream_t stream, int phase_mask) {
+  const size_t nk = (size_t)pb.T * pb.Hkv * pb.d;
+  const float c = pb.scale * kLog2e;
+  // 1. D and zeroed dK / dV accumulators
   if (phase_mask & 1) {
     const long long lanes = (long long)pb.T * pb.Hq * (pb.d / 8);
     dim3 grid((unsigned)((lanes + 255) / 256));
@@ -434,31 +531,39 @@ hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const voi
     else
       hipLaunchKernelGGL(pre_kernel<64>, grid, dim3(256), 0, stream, (const u16*)o,
                          (const u16*)dO, delta, pb.T, pb.Hq);
-    hipLaunchKernelGGL(zero_kernel, dim3(stream_grid(nq / 4)), dim3(256), 0, stream,
-                       (float4*)dq_acc, nq / 4);
     hipLaunchKernelGGL(zero_kernel, dim3(stream_grid(nk / 4)), dim3(256), 0, stream,
                        (float4*)dk_acc, nk / 4);
     hipLaunchKernelGGL(zero_kernel, dim3(stream_grid(nk / 4)), dim3(256), 0, stream,
                        (float4*)dv_acc, nk / 4);
   }
-  // 2. main
+  // 2. dK / dV (key-stationary)
   if ((phase_mask & 2) && n_items > 0) {
     HeadMap hm = make_headmap(n_items, pb.Hkv);
     dim3 grid(headmap_grid(hm)), block(64 * kBwdWaves);
-    const float c = pb.scale * kLog2e;
     if (pb.d == 128)
-      hipLaunchKernelGGL((main_kernel<128, kBwdWaves>), grid, block, 0, stream, (const u16*)q,
-                         (const u16*)k, (const u16*)v, (const u16*)dO, lse, delta, dq_acc,
-                         dk_acc, dv_acc, items_dev, hm, pb.T, pb.Hq, pb.Hkv, c);
+      hipLaunchKernelGGL((dkv_kernel<128>), grid, block, 0, stream, (const u16*)q,
+                         (const u16*)k, (const u16*)v, (const u16*)dO, lse, delta, dk_acc, dv_acc,
+                         items_dev, hm, pb.T, pb.Hq, pb.Hkv, c);
     else
-      hipLaunchKernelGGL((main_kernel<64, kBwdWaves>), grid, block, 0, stream, (const u16*)q,
-                         (const u16*)k, (const u16*)v, (const u16*)dO, lse, delta, dq_acc,
-                         dk_acc, dv_acc, items_dev, hm, pb.T, pb.Hq, pb.Hkv, c);
+      hipLaunchKernelGGL((dkv_kernel<64>), grid, block, 0, stream, (const u16*)q,
+                         (const u16*)k, (const u16*)v, (const u16*)dO, lse, delta, dk_acc, dv_acc,
+                         items_dev, hm, pb.T, pb.Hq, pb.Hkv, c);
   }
-  // 3. convert
+  // 8. dQ (query-stationary), written directly as bf16
+  if ((phase_mask & 8) && n_qitems > 0) {
+    HeadMap hm = make_headmap(n_qitems, pb.Hq);
+    dim3 grid(headmap_grid(hm)), block(64 * kDqWaves);
+    if (pb.d == 128)
+      hipLaunchKernelGGL((dq_kernel<128>), grid, block, 0, stream, (const u16*)q, (const u16*)k,
+                         (const u16*)v, (const u16*)dO, lse, delta, (u16*)dQ, qitems_dev, hm, pb.T,
+                         pb.Hq, pb.Hkv, c, pb.scale);
+    else
+      hipLaunchKernelGGL((dq_kernel<64>), grid, block, 0, stream, (const u16*)q, (const u16*)k,
+                         (const u16*)v, (const u16*)dO, lse, delta, (u16*)dQ, qitems_dev, hm, pb.T,
+                         pb.Hq, pb.Hkv, c, pb.scale);
+  }
+  // 3. dK, dV to bf16
   if (phase_mask & 4) {
-    hipLaunchKernelGGL(convert_kernel, dim3(stream_grid(nq / 4)), dim3(256), 0, stream,
-                       (const float4*)dq_acc, (uint2*)dQ, nq / 4, pb.scale);
     hipLaunchKernelGGL(convert_kernel, dim3(stream_grid(nk / 4)), dim3(256), 0, stream,
                        (const float4*)dk_acc, (uint2*)dK, nk / 4, pb.scale);
     hipLaunchKernelGGL(convert_kernel, dim3(stream_grid(nk / 4)), dim3(256), 0, stream,

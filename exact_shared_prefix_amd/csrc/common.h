@@ -42,9 +42,12 @@ struct FwdItem { int r0, r1, a_end, b_start; };
 // and the scheduler never pairs a response tile with foreign rows).
 struct BwdItem { int kb, ke, r0, r1; };
 
-// Backward workgroup shape: kBwdWaves waves of 32 keys each.
+// dK/dV workgroup: kBwdWaves waves of 32 keys each.
 constexpr int kBwdWaves = 8;
 constexpr int kBwdKeys = 32 * kBwdWaves;
+// dQ workgroup: kDqWaves waves of 32 query rows.
+constexpr int kDqWaves = 8;
+constexpr int kDqRows = 32 * kDqWaves;
 
 // Launch-time block -> (item, head) decomposition that keeps each head group
 // on one XCD (workgroups are dealt to the 8 XCDs round-robin by block id).

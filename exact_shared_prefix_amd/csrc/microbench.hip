@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void lds_b128_deep_kernel(uint32_t* out, int i
 #pragma unroll
     for (int u = 0; u < 16; ++u) v[u] = buf[(idx + u * 128) & 2047];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) acc ^= v[u].x ^ v[u].w;
+    for (int u = 0; u < 16; ++u) acc += v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
     idx = (idx + 64) & 2047;
   }
   out[blockIdx.x * 256 + threadIdx.x] = acc;

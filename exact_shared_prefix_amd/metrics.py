@@ -36,6 +36,14 @@ def useful_flops(P: int, lengths: Sequence[int], Hq: int, d: int) -> dict:
     return {"fwd": 4 * d * Hq * n, "bwd": 10 * d * Hq * n, "total": 14 * d * Hq * n}
 
 
+def kernel_flops(P: int, lengths: Sequence[int], Hq: int, d: int) -> dict:
+    """Algorithmic FLOPs each kernel executes on attended pairs: the forward
+    (S, PV), the key-stationary dK/dV pass (S, dP, dV, dK) and the
+    query-stationary dQ pass (S, dP recomputed, dQ)."""
+    n = pairs(P, lengths)
+    return {"fwd_kernel": 4 * d * Hq * n, "dkv_kernel": 8 * d * Hq * n, "dq_kernel": 6 * d * Hq * n}
+
+
 def tokens(P: int, lengths: Sequence[int]) -> tuple[int, int]:
     """(packed, replicated) token counts; their ratio is rho = N(P+R)/(P+NR)."""
     return P + sum(lengths), sum(P + int(r) for r in lengths)

@@ -69,9 +69,9 @@ typedef enum {
 size_t dualkv_fwd_workspace_bytes(int P, int R, int N, const int32_t* offsets,
                                   int Hq, int Hkv, int d);
 
-/* Workspace dualkv_bwd needs: the work list, D = rowsum(dO*O) [Hq][T] fp32
- * and fp32 accumulators for dQ [T][Hq][d], dK and dV [T][Hkv][d].
- * 0 if the arguments are invalid. */
+/* Workspace dualkv_bwd needs: the two work lists, D = rowsum(dO*O) [Hq][T]
+ * fp32, and fp32 accumulators for dK and dV [T][Hkv][d] (dQ is written
+ * directly). 0 if the arguments are invalid. */
 size_t dualkv_bwd_workspace_bytes(int P, int R, int N, const int32_t* offsets,
                                   int Hq, int Hkv, int d, int deterministic);
 
@@ -94,13 +94,15 @@ dualkv_status dualkv_bwd(const void* q, const void* k, const void* v, const void
                          int Hq, int Hkv, int d, float softmax_scale, int deterministic,
                          void* workspace, size_t workspace_bytes, void* stream);
 
-/* The backward of dualkv_bwd split into its three stream-ordered phases, so a
+/* The backward of dualkv_bwd split into its stream-ordered phases, so a
  * caller can time or interleave them: bit 1 = preprocess (D = rowsum(dO*O),
- * zeroed fp32 accumulators in the workspace), bit 2 = main (the two-region
- * KV-stationary pass, atomics into the accumulators), bit 4 = finish (fp32
- * accumulators -> bf16 dQ, dK, dV). Same arguments and checks as dualkv_bwd;
- * dualkv_bwd is phase_mask 7. Phases must run in order on the same workspace
- * with the same arguments; a mask of 0 or above 7 is DUALKV_ERR_INVALID_ARG. */
+ * zeroed fp32 dK, dV accumulators in the workspace), bit 2 = key-stationary
+ * dK, dV pass (two KV regions, fp32 atomics into the accumulators), bit 8 =
+ * query-stationary dQ pass (writes dQ), bit 4 = finish (accumulators -> bf16
+ * dK, dV). Same arguments and checks as dualkv_bwd, which is phase_mask 15.
+ * Bit 1 must run before bits 2, 4 and 8, and bit 2 before bit 4, on the same
+ * workspace with the same arguments; a mask of 0 or above 15 is
+ * DUALKV_ERR_INVALID_ARG. */
 dualkv_status dualkv_bwd_phases(const void* q, const void* k, const void* v, const void* o,
                                 const float* lse, const void* dO, void* dQ, void* dK, void* dV,
                                 int P, int R, int N, const int32_t* offsets,

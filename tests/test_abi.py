@@ -105,8 +105,9 @@ def test_bwd_rejects_bad_arguments(lib, kw, status):
     assert _bwd(lib, **kw) == status
 
 
-@pytest.mark.parametrize("mask,status", [(0, ERR_INVALID_ARG), (8, ERR_INVALID_ARG),
-                                         (-1, ERR_INVALID_ARG), (2, ERR_WORKSPACE)])
+@pytest.mark.parametrize("mask,status", [(0, ERR_INVALID_ARG), (16, ERR_INVALID_ARG),
+                                         (-1, ERR_INVALID_ARG), (2, ERR_WORKSPACE),
+                                         (8, ERR_WORKSPACE)])
 def test_bwd_phases_rejects_bad_mask(lib, mask, status):
     r = lib.dualkv_bwd_phases(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 8, 2, None,
                               4, 2, 128, 0.1, 0, FAKE, 16, None, mask)
@@ -119,8 +120,9 @@ def test_workspace_sizes(lib):
     nb = binding.bwd_workspace_bytes(pk, 4, 2, 64)
     assert nf >= 16 and nf % 256 == 0
     T = pk.T
-    # bwd holds at least D [Hq,T] and fp32 dQ/dK/dV accumulators
-    assert nb >= 4 * (4 * T + T * 4 * 64 + 2 * T * 2 * 64)
+    # bwd holds at least D [Hq,T] and fp32 dK/dV accumulators (dQ is written directly)
+    assert nb >= 4 * (4 * T + 2 * T * 2 * 64)
+    assert nb < 4 * (4 * T + 2 * T * 2 * 64) + 4 * T * 4 * 64
     with pytest.raises(binding.DualKVError):
         binding.bwd_workspace_bytes(pk, 4, 2, 64, deterministic=True)
     with pytest.raises(binding.DualKVError):
