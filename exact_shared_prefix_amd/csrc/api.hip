@@ -28,7 +28,6 @@ using namespace dkv;
 
 namespace {
 
-constexpr int kFwdRows = 128;   // query rows per forward workgroup
 constexpr int kBwdChunk = 1024; // query rows per backward work item (grid of row chunks)
 constexpr size_t kAlign = 256;
 

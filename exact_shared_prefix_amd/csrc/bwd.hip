@@ -18,14 +18,8 @@
 //                  (fp32 atomics run at a fixed rate per lane on this GPU, and
 //                  a key-stationary dQ would need one per row, d and key tile).
 //  3. convert_kernel: fp32 dK, dV -> bf16 (dK scaled by the softmax scale).
-//
-// MFMA operands staged in LDS are kept "fragment-native": one operand of a
-// wave (64 lanes x 8 bf16) is 1 KB with lane l's 16 bytes at byte 16 l, so
-// every fragment read or write is one lane-linear 16-byte access. Operands
-// needed transposed (Q^T, dO^T for dV, dK; K^T for dQ) are produced by an
-// MFMA against a unit fragment, which moves a 32 x 32 block into accumulator
-// layout exactly (one nonzero product per element).
 #include "common.h"
+#include "frag.h"
 
 namespace dkv {
 
@@ -62,81 +56,6 @@ __global__ __launch_bounds__(256) void pre_kernel(const u16* __restrict__ o,
 __global__ __launch_bounds__(256) void zero_kernel(float4* __restrict__ p, size_t n4) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256)
     p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-}
-
-// ---------------------------------------------------------- fragments --
-constexpr int kFrag = 512;  // u16 elements per fragment
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void glb_void;
-
-// Direct global -> LDS copy of 16 (4) bytes per lane: lane l's bytes land at
-// lds_base + 16 l (4 l); lds_base is the same for the whole wave. Written as
-// inline assembly so that the compiler does not treat every later LDS read
-// as possibly overwritten by the copy (it would wait for all outstanding
-// memory operations before each one); the kernel waits for the copies itself.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
-  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const void* g, void* lds_base) {
-  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m) : "memory", "m0");
-}
-
-__device__ __forceinline__ bf16x8 frag_ld(const u16* f, int lane) { return lds_b128(f + 8 * lane); }
-__device__ __forceinline__ void frag_st(u16* f, int lane, bf16x8 v) {
-  Frag x{v};
-  *reinterpret_cast<uint4*>(f + 8 * lane) = x.u;
-}
-
-// B operand holding a single 1.0 at k-slot e_on (0..7) for lanes with on set.
-// Used as the right factor of an MFMA that copies its left operand into the
-// accumulator layout, i.e. transposes a fragment exactly.
-__device__ __forceinline__ bf16x8 unit_frag(bool on, int e_on) {
-  const uint32_t one = 0x3f80u << (16 * (e_on & 1));
-  const int wsel = e_on >> 1;
-  Frag f;
-  f.u.x = (on && wsel == 0) ? one : 0u;
-  f.u.y = (on && wsel == 1) ? one : 0u;
-  f.u.z = (on && wsel == 2) ? one : 0u;
-  f.u.w = (on && wsel == 3) ? one : 0u;
-  return f.v;
-}
-
-// k-slot e of lane half hl in a P / dS fragment (and in every operand that is
-// paired with one) stands for query row 8 (e / 4) + 4 hl + e % 4 of its
-// 16-row step: the row order of the 32x32 accumulator.
-//
-// Transpose of a 32 x 32 block X held as two A-operand fragments (k = columns
-// 0..15 and 16..31 in natural order): returns X in accumulator layout (lane ->
-// column, register r -> row 8 (r/4) + 4 hl + r%4).
-__device__ __forceinline__ f32x16 xpose_nat(bf16x8 a0, bf16x8 a1, int lane) {
-  asm volatile("" : "+v"(lane));
-  const int n = lane & 31, hl = lane >> 5;
-  const bool mine = hl == ((n >> 3) & 1);
-  f32x16 d = mfma32(a0, unit_frag(mine && (n >> 4) == 0, n & 7), f32x16{});
-  return mfma32(a1, unit_frag(mine && (n >> 4) == 1, n & 7), d);
-}
-__device__ __forceinline__ void pack2(const f32x16& x, bf16x8& f0, bf16x8& f1) {
-  f0 = pack_bf16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
-  f1 = pack_bf16x8(x[8], x[9], x[10], x[11], x[12], x[13], x[14], x[15]);
-}
-
-__device__ __forceinline__ float bf16_elem(const bf16x8& f, int e) {
-  Frag x{f};
-  const uint32_t w = e < 2 ? x.u.x : e < 4 ? x.u.y : e < 6 ? x.u.z : x.u.w;
-  return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
-}
-
-// Wait until at most N vector-memory operations of this wave (the direct
-// copies above included) are outstanding, then an LDS barrier.
-template <int N>
-__device__ __forceinline__ void vm_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 // -------------------------------------------------------------------- dKV --

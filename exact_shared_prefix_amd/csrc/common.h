@@ -42,6 +42,9 @@ struct FwdItem { int r0, r1, a_end, b_start; };
 // and the scheduler never pairs a response tile with foreign rows).
 struct BwdItem { int kb, ke, r0, r1; };
 
+// Forward workgroup: kFwdWaves waves of 32 query rows.
+constexpr int kFwdWaves = 8;
+constexpr int kFwdRows = 32 * kFwdWaves;
 // dK/dV workgroup: kBwdWaves waves of 32 keys each.
 constexpr int kBwdWaves = 8;
 constexpr int kBwdKeys = 32 * kBwdWaves;
