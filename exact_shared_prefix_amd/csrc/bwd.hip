@@ -169,6 +169,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk)
         sacc = mfma32(frag_ld(qa + kk * kFrag, lane), frag_ld(kfl + kk * kFrag, lane), sacc);
+      pipelined_mfma<NKK, 2, 2>();
       const float* lw = ld + 64 * w;
       if ((kw + 31 > qb) || (kw + 32 > it.ke) || (qb + BQ > it.r1)) {
 #pragma unroll
@@ -196,6 +197,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
       f32x16 dpacc = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) dpacc = mfma32(frag_ld(oa + kk * kFrag, lane), vf[kk], dpacc);
+      pipelined_mfma<NKK, 1, 4>();
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const float4 d4 = *reinterpret_cast<const float4*>(lw + 32 + 8 * g4 + 4 * hl);
@@ -217,10 +219,12 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) dvacc[dt] = mfma32(pf[ks], frag_ld(OT + (2 * dt + ks) * kFrag, lane), dvacc[dt]);
+      pipelined_mfma<2 * NDT, 1, 4>();
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) dkacc[dt] = mfma32(sf[ks], frag_ld(QT + (2 * dt + ks) * kFrag, lane), dkacc[dt]);
+      pipelined_mfma<2 * NDT, 1, 4>();
     }
   };
 
@@ -364,6 +368,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
       f32x16 sacc = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) sacc = mfma32(frag_ld(ka + (kb2 * NKK + kk) * kFrag, lane), qf[kk], sacc);
+      pipelined_mfma<NKK, 1, 4>();
       const bool need_mask = (k0 + 31 > t0) || (k0 + 32 > ke);
       if (need_mask) {
 #pragma unroll
@@ -381,6 +386,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
       f32x16 dpacc = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) dpacc = mfma32(frag_ld(va + (kb2 * NKK + kk) * kFrag, lane), of[kk], dpacc);
+      pipelined_mfma<NKK, 1, 4>();
 #pragma unroll
       for (int r = 0; r < 16; ++r) dpacc[r] = bf16_elem(pf[r >> 3], r & 7) * (dpacc[r] - dl);
       bf16x8 sf[2];
@@ -390,6 +396,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
           dqacc[dt] = mfma32(frag_ld(KT + ((kb2 * NDT + dt) * 2 + ks) * kFrag, lane), sf[ks], dqacc[dt]);
+      pipelined_mfma<2 * NDT, 1, 4>();
     }
   };
 

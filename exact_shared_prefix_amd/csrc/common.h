@@ -151,6 +151,22 @@ __device__ __forceinline__ void reads_then_mfma() {
   __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);  // MFMA
 }
 
+// Scheduling hint for the region that ends here: a chain of NM MFMAs whose
+// operands come from NR = RPM * NM LDS reads is issued with the reads DEPTH
+// MFMAs ahead of their use (DEPTH * RPM reads first, then RPM reads after each
+// MFMA), so each MFMA waits only for reads issued long before it.
+template <int NM, int RPM, int DEPTH>
+__device__ __forceinline__ void pipelined_mfma() {
+  static_assert(DEPTH >= 1 && DEPTH <= NM, "depth");
+  __builtin_amdgcn_sched_group_barrier(0x100, DEPTH * RPM, 0);
+#pragma unroll
+  for (int i = 0; i < NM - DEPTH; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, DEPTH, 0);
+}
+
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS
 // operations, then s_barrier; the memory clobber keeps the compiler from
 // moving memory accesses across it. Unlike __syncthreads() it does not wait
@@ -163,11 +179,16 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// max / sum of x over lanes l and l ^ 32. v_permlane32_swap exchanges the
+// two 32-lane halves between its two operands; with x in both, the pair
+// holds x(l) and x(l ^ 32) in some order on every lane.
 __device__ __forceinline__ float wave_swap32_max(float x) {
-  return fmaxf(x, __shfl_xor(x, 32));
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float wave_swap32_sum(float x) {
-  return x + __shfl_xor(x, 32);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 }  // namespace dkv

@@ -118,15 +118,15 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void fwd_kernel(
     if (!wave_rows || kb > t0 + 31) return;   // every key of the tile lies after this wave's rows
 
     // S^T[key][query]: block kb2, register r <-> key kb + 32 kb2 + 8 (r/4) + 4 hl + r%4
-    f32x16 s[2];
+    f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      s[kb2] = f32x16{};
+    for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) s[kb2] = mfma32(frag_ld(ka + (kb2 * NKK + kk) * kFrag, lane), qf[kk], s[kb2]);
-    }
+      for (int kb2 = 0; kb2 < 2; ++kb2) s[kb2] = mfma32(frag_ld(ka + (kb2 * NKK + kk) * kFrag, lane), qf[kk], s[kb2]);
+    pipelined_mfma<2 * NKK, 1, 4>();
+
+    // masked scores become -inf and their exp2 exact zeros
     const bool need_mask = (kb + BK > ke) || (kb + BK - 1 > t0);
-    float mx = -INFINITY;
     if (need_mask) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
@@ -134,14 +134,13 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void fwd_kernel(
         for (int r = 0; r < 16; ++r) {
           const int j = kb + 32 * kb2 + 8 * (r >> 2) + 4 * hl + (r & 3);
           if (j >= ke || j > t) s[kb2][r] = -INFINITY;
-          mx = fmaxf(mx, s[kb2][r]);
         }
-    } else {
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb2][r]);
     }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb2][r]);
     mx = wave_swap32_max(mx);
     // lazy rescaling: the reference max only moves when some row's max exceeds
     // it by more than 8 (log2 units); O / l and the LSE do not depend on it
@@ -160,6 +159,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void fwd_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float x = fast_exp2(fmaf(s[kb2][r], c, -m2));
+        // explicit zero: with a softmax scale of 0, -inf * c is not -inf
         if (need_mask && s[kb2][r] == -INFINITY) x = 0.f;
         s[kb2][r] = x;
         ps += x;
@@ -170,12 +170,13 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void fwd_kernel(
 
     // O^T[d][q] += V^T[d][key] P^T[key][q]
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+    for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+        for (int dt = 0; dt < NDT; ++dt)
           oacc[dt] = mfma32(frag_ld(VT + ((kb2 * NDT + dt) * 2 + ks) * kFrag, lane), pf[kb2][ks], oacc[dt]);
+    pipelined_mfma<4 * NDT, 1, 4>();
   };
 
   // The tile loop alternates between two statically distinct buffer sets.
