@@ -140,7 +140,31 @@ __global__ __launch_bounds__(256) void copy_kernel(const uint4* __restrict__ src
   for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
 }
 
+// fp32 atomic-add throughput: each wave adds 1.0 to 2 rows x 32 consecutive
+// floats per instruction (the pattern of an accumulator tile in accumulator
+// layout), 16 instructions per iteration, rows spread over `rows` rows of a
+// 128-float pitch. Every address stays below rows * 128.
+__global__ __launch_bounds__(256) void atomic_kernel(float* buf, int rows, int iters) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const unsigned r0 = (unsigned)(blockIdx.x * 4 + w) * 97u;
+  for (int it = 0; it < iters; ++it) {
+    const unsigned row = (r0 + (unsigned)it * 8u) % (unsigned)(rows - 32);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const unsigned rr = row + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+      unsafeAtomicAdd(buf + (size_t)rr * 128 + (lane & 31), 1.0f);
+    }
+  }
+}
+
 extern "C" {
+
+// blocks x 256 threads x iters x 16 atomic lanes into buf[rows * 128] (rows >= 64).
+int dkv_mb_atomic(int blocks, int iters, float* buf, int rows, void* stream) {
+  if (rows < 64) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(atomic_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, buf, rows, iters);
+  return (int)hipGetLastError();
+}
 
 // Copies n16 16-byte words from src to dst (device pointers, no overlap).
 int dkv_mb_copy(const void* src, void* dst, long n16, void* stream) {

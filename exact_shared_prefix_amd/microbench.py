@@ -4,6 +4,7 @@ mfma_tflops(): sustained dense bf16 MFMA rate (32x32x16, register operands,
 four independent chains per wave, 8 waves per CU on every CU).
 lds_bytes_per_clk(): LDS read bandwidth per CU for 16-byte reads and for
 8-byte transpose reads, from the measured time and the GPU's clock.
+atomic_lanes_per_s(): sustained fp32 atomic-add rate (lanes per second).
 """
 from __future__ import annotations
 
@@ -28,6 +29,8 @@ def _load():
             fn = getattr(_lib, name)
             fn.restype = ctypes.c_int
             fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        _lib.dkv_mb_atomic.restype = ctypes.c_int
+        _lib.dkv_mb_atomic.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
         _lib.dkv_mb_copy.restype = ctypes.c_int
         _lib.dkv_mb_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p]
     return _lib
@@ -81,6 +84,21 @@ def copy(nbytes: int, reps: int = 3) -> dict:
             "gbs": 2 * n16 * 16 / best / 1e9}
 
 
+def atomic_lanes_per_s(rows: int = 139264 * 32, blocks: int = 2048, iters: int = 50) -> float:
+    """Sustained fp32 atomic-add lanes per second into a [rows][128] fp32 buffer."""
+    lib = _load()
+    buf = torch.zeros(rows * 128, dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream()
+    assert lib.dkv_mb_atomic(blocks, 2, buf.data_ptr(), rows, s.cuda_stream) == 0
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    assert lib.dkv_mb_atomic(blocks, iters, buf.data_ptr(), rows, s.cuda_stream) == 0
+    e1.record(s)
+    torch.cuda.synchronize()
+    return blocks * 256 * iters * 16 / (e0.elapsed_time(e1) * 1e-3)
+
+
 def mfma_tflops(iters: int = 4096) -> float:
     """Best of: 8 waves/CU x 4 chains, and 4 waves/CU x 8 chains."""
     lib = _load()
@@ -110,4 +128,5 @@ def lds_bytes_per_clk(iters: int = 4096) -> dict:
 
 if __name__ == "__main__":
     print({"cus": cu_count(), "clock_hz": clock_hz(), "mfma_bf16_tflops": mfma_tflops(),
-           "lds_bytes_per_clk_per_cu": lds_bytes_per_clk()})
+           "lds_bytes_per_clk_per_cu": lds_bytes_per_clk(),
+           "fp32_atomic_lanes_per_s": atomic_lanes_per_s()})
