@@ -28,7 +28,7 @@ using namespace dkv;
 
 namespace {
 
-constexpr int kBwdChunk = 1024; // query rows per backward work item (grid of row chunks)
+constexpr int kBwdChunk = 2048; // query rows per dK/dV work item (grid of row chunks)
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }

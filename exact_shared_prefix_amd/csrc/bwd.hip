@@ -147,7 +147,6 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
                   float* ldn) {
     const int qb = it.r0 + (st / G) * BQ;
     vm_barrier<0>();   // this step's copies landed; every wave is done with the last step
-    if (st + 1 < nsteps) stage(st + 1, qan, oan, ldn);
 
     // Q^T (job < NDT) and dO^T B fragments of d tile job % NDT
     if (w < 2 * NDT) {
@@ -198,6 +197,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) dpacc = mfma32(frag_ld(oa + kk * kFrag, lane), vf[kk], dpacc);
       pipelined_mfma<NKK, 1, 4>();
+      if (st + 1 < nsteps) stage(st + 1, qan, oan, ldn);
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const float4 d4 = *reinterpret_cast<const float4*>(lw + 32 + 8 * g4 + 4 * hl);
@@ -211,6 +211,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
       }
       pack2(dpacc, sf[0], sf[1]);
     }
+    if (!active && st + 1 < nsteps) stage(st + 1, qan, oan, ldn);
     lds_barrier();   // Q^T, dO^T fragments complete
 
     if (active) {
