@@ -94,7 +94,8 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
   if (!headmap_decode(hm, blockIdx.x, item_id, g)) return;
   const BwdItem it = items[item_id];
   const int G = Hq / Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept in a scalar register
   const int hl = lane >> 5, l32 = lane & 31;
   const size_t qrow = (size_t)Hq * D, krow = (size_t)Hkv * D;
   const int kw = it.kb + 32 * w;   // first key of this wave
@@ -288,7 +289,8 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
   const FwdItem it = items[item_id];
   const int G = Hq / Hkv;
   const int g = h / G;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept in a scalar register
   const int hl = lane >> 5, l32 = lane & 31;
   const int t0 = it.r0 + 32 * w;   // first query row of this wave
   const int t = t0 + l32;          // this lane's query row

@@ -47,7 +47,8 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void fwd_kernel(
   const FwdItem it = items[item_id];
   const int G = Hq / Hkv;
   const int g = h / G;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept in a scalar register
   const int hl = lane >> 5, l32 = lane & 31;
   const int t0 = it.r0 + 32 * w;   // first query row of this wave
   const int t = t0 + l32;          // this lane's query row
