@@ -125,6 +125,8 @@ def time_steps(q, k, v, do, pk, scale, steps, warmup, phase_events=True):
     if phase_events:
         def avg(a, b):
             return sum(e[a].elapsed_time(e[b]) for e in evs) / steps
+        per = sorted(e[0].elapsed_time(e[5]) for e in evs)
+        res.update(min_ms_per_step=per[0], median_ms_per_step=per[len(per) // 2])
         res.update(fwd_ms=avg(0, 1), bwd_pre_ms=avg(1, 2), bwd_dkv_ms=avg(2, 3),
                    bwd_dq_ms=avg(3, 4), bwd_finish_ms=avg(4, 5), bwd_ms=avg(1, 5))
     del o, lse, dq, dk, dv, wsf, wsb
@@ -209,6 +211,7 @@ def main() -> int:
     ap.add_argument("--no-replicated", action="store_true", help="skip the unshared-layout run")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-mfma-peak", action="store_true", help="skip the measured MFMA peak")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -303,6 +306,16 @@ def main() -> int:
         cpu = cpu_baseline(inp, args.cpu_seconds)
         log(f"[bench] CPU oracle: {cpu['value']:.4g} TFLOP/s on {cpu['cores']} threads")
 
+    mfma_peak = None
+    if not args.no_mfma_peak:
+        from exact_shared_prefix_amd import microbench
+        meas = microbench.mfma_tflops()
+        mfma_peak = {"measured_tflops": meas, "unit": "TFLOP/s",
+                     "kernel": "mfma_rate_kernel / mfma_rate8_kernel (register operands, every CU)",
+                     "value_frac_of_measured": value / meas,
+                     "dominant_kernel_frac_of_measured": ach / meas}
+        log(f"[bench] measured bf16 MFMA peak {meas:.0f} TFLOP/s")
+
     packed_tok, rep_tok = metrics.tokens(P, L)
     out = {
         "metric": METRIC,
@@ -328,6 +341,7 @@ def main() -> int:
         "kernels": other,
         "roofline": roofline,
         "peak_hbm_gb": peak_packed / 1e9,
+        "mfma_peak": mfma_peak,
         "replicated": replicated,
         "cpu_baseline": cpu,
     }

@@ -134,8 +134,7 @@ def bwd_workspace_bytes(pk: Packing, Hq: int, Hkv: int, d: int, deterministic: b
                                           int(deterministic))
     pk._ws[key] = n
     if n == 0:
-        raise DualKVError(ERR_UNSUPPORTED if deterministic else ERR_INVALID_ARG,
-                          "invalid problem shape or unsupported mode")
+        raise DualKVError(ERR_INVALID_ARG, "invalid problem shape")
     return n
 
 

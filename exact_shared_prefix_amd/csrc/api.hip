@@ -20,8 +20,9 @@ hipError_t launch_fwd(const Problem& pb, const void* q, const void* k, const voi
 hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dO, void* dQ, void* dK,
                       void* dV, const BwdItem* items_dev, int n_items, const FwdItem* qitems_dev,
-                      int n_qitems, float* delta, float* dk_acc, float* dv_acc,
-                      hipStream_t stream, int phase_mask);
+                      int n_qitems, float* delta, float* dk_acc, float* dv_acc, float* part,
+                      const int* tile_off, const int* tile_items, int n_tiles, hipStream_t stream,
+                      int phase_mask);
 }  // namespace dkv
 
 using namespace dkv;
@@ -138,8 +139,10 @@ std::vector<FwdItem> fwd_items(const Problem& pb, int rows = kFwdRows) {
 // dK/dV work list: kBwdKeys-key tiles, each paired with the rows that attend it
 // (all later rows for a prompt tile, the later rows of its own response for a
 // response tile), cut on a fixed grid of kBwdChunk-row chunks. Items are
-// ordered chunk-major so workgroups running together share query rows.
-std::vector<BwdItem> bwd_items(const Problem& pb) {
+// ordered chunk-major so workgroups running together share query rows. With
+// tiles != null, also returns each tile's items (ascending) as a CSR list.
+struct TileLists { std::vector<int> off, items; };
+std::vector<BwdItem> bwd_items(const Problem& pb, TileLists* tl_out = nullptr) {
   struct Tile { int kb, ke, rend; };
   std::vector<Tile> tiles;
   for (int kb = 0; kb < pb.P; kb += kBwdKeys) tiles.push_back({kb, std::min(pb.P, kb + kBwdKeys), pb.T});
@@ -148,29 +151,51 @@ std::vector<BwdItem> bwd_items(const Problem& pb) {
     for (int kb = a; kb < b; kb += kBwdKeys) tiles.push_back({kb, std::min(b, kb + kBwdKeys), b});
   }
   std::vector<BwdItem> items;
+  std::vector<std::vector<int>> per_tile(tiles.size());
   const int nchunks = (pb.T + kBwdChunk - 1) / kBwdChunk;
   for (int cidx = 0; cidx < nchunks; ++cidx) {
     const int c0 = cidx * kBwdChunk, c1 = std::min(pb.T, c0 + kBwdChunk);
-    for (const Tile& tl : tiles) {
+    for (size_t ti = 0; ti < tiles.size(); ++ti) {
+      const Tile& tl = tiles[ti];
       const int r0 = std::max(c0, tl.kb), r1 = std::min(c1, tl.rend);
-      if (r0 < r1) items.push_back({tl.kb, tl.ke, r0, r1});
+      if (r0 < r1) {
+        per_tile[ti].push_back((int)items.size());
+        items.push_back({tl.kb, tl.ke, r0, r1});
+      }
+    }
+  }
+  if (tl_out) {
+    tl_out->off.assign(1, 0);
+    tl_out->items.clear();
+    for (const auto& v : per_tile) {
+      tl_out->items.insert(tl_out->items.end(), v.begin(), v.end());
+      tl_out->off.push_back((int)tl_out->items.size());
     }
   }
   return items;
 }
 
 struct BwdLayout {
-  size_t items, qitems, delta, dk, dv, total;
+  size_t items, qitems, delta, dk, dv, part, tile_off, tile_items, total;
 };
 
-BwdLayout bwd_layout(const Problem& pb, size_t n_items, size_t n_qitems) {
-  BwdLayout L;
+// Atomic mode: fp32 dK, dV accumulators [T][Hkv][d]. Deterministic mode:
+// per-item partials [n_items][Hkv][2][kBwdKeys][d] and the tile CSR lists.
+BwdLayout bwd_layout(const Problem& pb, size_t n_items, size_t n_qitems, bool det,
+                     size_t n_tiles) {
+  BwdLayout L{};
   size_t off = 0;
   L.items = off;  off = align_up(off + n_items * sizeof(BwdItem));
   L.qitems = off; off = align_up(off + n_qitems * sizeof(FwdItem));
   L.delta = off;  off = align_up(off + (size_t)pb.Hq * pb.T * sizeof(float));
-  L.dk = off;    off = align_up(off + (size_t)pb.T * pb.Hkv * pb.d * sizeof(float));
-  L.dv = off;    off = align_up(off + (size_t)pb.T * pb.Hkv * pb.d * sizeof(float));
+  if (det) {
+    L.part = off;       off = align_up(off + n_items * pb.Hkv * 2 * (size_t)kBwdKeys * pb.d * sizeof(float));
+    L.tile_off = off;   off = align_up(off + (n_tiles + 1) * sizeof(int));
+    L.tile_items = off; off = align_up(off + n_items * sizeof(int));
+  } else {
+    L.dk = off; off = align_up(off + (size_t)pb.T * pb.Hkv * pb.d * sizeof(float));
+    L.dv = off; off = align_up(off + (size_t)pb.T * pb.Hkv * pb.d * sizeof(float));
+  }
   L.total = off;
   return L;
 }
@@ -189,10 +214,11 @@ size_t dualkv_fwd_workspace_bytes(int P, int R, int N, const int32_t* offsets, i
 size_t dualkv_bwd_workspace_bytes(int P, int R, int N, const int32_t* offsets, int Hq, int Hkv,
                                   int d, int deterministic) {
   Problem pb;
-  if (deterministic) return 0;
   if (check_shape(P, R, N, offsets, Hq, Hkv, d, pb) != DUALKV_OK) return 0;
-  return bwd_layout(pb, std::max<size_t>(1, bwd_items(pb).size()),
-                    std::max<size_t>(1, fwd_items(pb, kDqRows).size())).total;
+  TileLists tl;
+  const size_t ni = bwd_items(pb, &tl).size();
+  return bwd_layout(pb, std::max<size_t>(1, ni), std::max<size_t>(1, fwd_items(pb, kDqRows).size()),
+                    deterministic != 0, tl.off.size() - 1).total;
 }
 
 dualkv_status dualkv_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int P,
@@ -229,22 +255,31 @@ dualkv_status dualkv_bwd_phases(const void* q, const void* k, const void* v, con
   dualkv_status st = check_shape(P, R, N, offsets, Hq, Hkv, d, pb);
   if (st != DUALKV_OK) return st;
   if (phase_mask < 1 || phase_mask > 15) return DUALKV_ERR_INVALID_ARG;
-  if (deterministic) return DUALKV_ERR_UNSUPPORTED;
   if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return DUALKV_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
       !aligned16(dO) || !aligned16(dQ) || !aligned16(dK) || !aligned16(dV))
     return DUALKV_ERR_INVALID_ARG;
   pb.scale = softmax_scale;
-  const std::vector<BwdItem> items = bwd_items(pb);
+  const bool det = deterministic != 0;
+  TileLists tl;
+  const std::vector<BwdItem> items = bwd_items(pb, &tl);
   const std::vector<FwdItem> qitems = fwd_items(pb, kDqRows);
-  const BwdLayout L = bwd_layout(pb, std::max<size_t>(1, items.size()), std::max<size_t>(1, qitems.size()));
+  const int n_tiles = (int)tl.off.size() - 1;
+  const BwdLayout L = bwd_layout(pb, std::max<size_t>(1, items.size()),
+                                 std::max<size_t>(1, qitems.size()), det, n_tiles);
   if (!workspace || workspace_bytes < L.total) return DUALKV_ERR_WORKSPACE;
   if (!aligned16(workspace)) return DUALKV_ERR_INVALID_ARG;
   if (pb.T == 0) return DUALKV_OK;
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((phase_mask & 2) && !items.empty() &&
+  // the dK/dV pass reads the item list, and so does the ordered reduction
+  const bool need_items = (phase_mask & 2) || (det && (phase_mask & 4));
+  if (need_items && !items.empty() &&
       upload(ws + L.items, items.data(), items.size() * sizeof(BwdItem), s) != hipSuccess)
+    return DUALKV_ERR_HIP;
+  if (det && (phase_mask & 4) && !items.empty() &&
+      (upload(ws + L.tile_off, tl.off.data(), tl.off.size() * sizeof(int), s) != hipSuccess ||
+       upload(ws + L.tile_items, tl.items.data(), tl.items.size() * sizeof(int), s) != hipSuccess))
     return DUALKV_ERR_HIP;
   if ((phase_mask & 8) && !qitems.empty() &&
       upload(ws + L.qitems, qitems.data(), qitems.size() * sizeof(FwdItem), s) != hipSuccess)
@@ -252,7 +287,11 @@ dualkv_status dualkv_bwd_phases(const void* q, const void* k, const void* v, con
   if (launch_bwd(pb, q, k, v, o, lse, dO, dQ, dK, dV, reinterpret_cast<const BwdItem*>(ws + L.items),
                  (int)items.size(), reinterpret_cast<const FwdItem*>(ws + L.qitems),
                  (int)qitems.size(), reinterpret_cast<float*>(ws + L.delta),
-                 reinterpret_cast<float*>(ws + L.dk), reinterpret_cast<float*>(ws + L.dv), s,
+                 det ? nullptr : reinterpret_cast<float*>(ws + L.dk),
+                 det ? nullptr : reinterpret_cast<float*>(ws + L.dv),
+                 det ? reinterpret_cast<float*>(ws + L.part) : nullptr,
+                 reinterpret_cast<const int*>(ws + L.tile_off),
+                 reinterpret_cast<const int*>(ws + L.tile_items), det ? n_tiles : 0, s,
                  phase_mask) != hipSuccess)
     return DUALKV_ERR_HIP;
   return DUALKV_OK;

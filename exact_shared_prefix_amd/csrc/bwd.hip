@@ -18,6 +18,9 @@
 //                  (fp32 atomics run at a fixed rate per lane on this GPU, and
 //                  a key-stationary dQ would need one per row, d and key tile).
 //  3. convert_kernel: fp32 dK, dV -> bf16 (dK scaled by the softmax scale).
+// Deterministic mode replaces the dK/dV atomics by per-item partials that
+// reduce_kernel sums in a fixed order (the dQ kernel has no atomics at all),
+// so the whole backward is bitwise reproducible.
 #include "common.h"
 #include "frag.h"
 
@@ -72,8 +75,8 @@ template <int D>
 __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const u16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
-    float* __restrict__ dk_acc, float* __restrict__ dv_acc, const BwdItem* __restrict__ items,
-    HeadMap hm, int T, int Hq, int Hkv, float c) {
+    float* __restrict__ dk_acc, float* __restrict__ dv_acc, float* __restrict__ part,
+    const BwdItem* __restrict__ items, HeadMap hm, int T, int Hq, int Hkv, float c) {
   constexpr int NW = kBwdWaves;
   constexpr int BQ = 32;
   constexpr int NKK = D / 16;     // A fragments per 32-row block
@@ -237,6 +240,20 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
     if (st + 1 < nsteps) step(st + 1, QA1, OA1, LD1, QA0, OA0, LD0);
   }
 
+  if (part) {
+    // deterministic mode: this item's partial dK, dV for all kBwdKeys keys
+    // ([item][g][key][d], dK then dV), summed in item order by reduce_kernel
+    float* pk = part + ((size_t)item_id * Hkv + g) * (size_t)(2 * kBwdKeys * D) + 32 * w * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kl = 8 * (r >> 2) + 4 * hl + (r & 3);
+        pk[kl * D + 32 * dt + l32] = dkacc[dt][r];
+        pk[(size_t)kBwdKeys * D + kl * D + 32 * dt + l32] = dvacc[dt][r];
+      }
+    return;
+  }
   // partial dK / dV of this chunk (where the N sequences' prompt gradients
   // meet); keys past the tile end add exact zeros to the tile's last key
   if (kw < it.ke) {
@@ -253,6 +270,42 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
         unsafeAtomicAdd(dvp + off, ok ? dvacc[dt][r] : 0.f);
       }
     }
+  }
+}
+
+// ------------------------------------------------------------- reduce --
+// Deterministic mode: for key tile `tile` and KV head g, sum the partials of
+// the tile's items in item order (fixed, so the result is bitwise
+// reproducible) and write dK = bf16(scale * sum), dV = bf16(sum).
+template <int D>
+__global__ __launch_bounds__(256) void reduce_kernel(
+    const float* __restrict__ part, const BwdItem* __restrict__ items,
+    const int* __restrict__ tile_off, const int* __restrict__ tile_items, u16* __restrict__ dK,
+    u16* __restrict__ dV, int Hkv, float scale) {
+  const int tile = blockIdx.x / Hkv, g = blockIdx.x % Hkv;
+  const int i0 = tile_off[tile], i1 = tile_off[tile + 1];
+  if (i0 >= i1) return;
+  const BwdItem first = items[tile_items[i0]];
+  const int nkeys = first.ke - first.kb;
+  const size_t krow = (size_t)Hkv * D;
+  for (int idx = threadIdx.x; idx < nkeys * D / 4; idx += 256) {
+    const int kl = (4 * idx) / D, dc = (4 * idx) % D;
+    float4 sk = make_float4(0.f, 0.f, 0.f, 0.f), sv = sk;
+    for (int i = i0; i < i1; ++i) {
+      const float* pk = part + ((size_t)tile_items[i] * Hkv + g) * (size_t)(2 * kBwdKeys * D) + kl * D + dc;
+      const float4 a = *reinterpret_cast<const float4*>(pk);
+      const float4 b = *reinterpret_cast<const float4*>(pk + (size_t)kBwdKeys * D);
+      sk.x += a.x; sk.y += a.y; sk.z += a.z; sk.w += a.w;
+      sv.x += b.x; sv.y += b.y; sv.z += b.z; sv.w += b.w;
+    }
+    const size_t o = (size_t)(first.kb + kl) * krow + (size_t)g * D + dc;
+    uint2 wk, wv;
+    wk.x = pack_bf16x2(sk.x * scale, sk.y * scale);
+    wk.y = pack_bf16x2(sk.z * scale, sk.w * scale);
+    wv.x = pack_bf16x2(sv.x, sv.y);
+    wv.y = pack_bf16x2(sv.z, sv.w);
+    *reinterpret_cast<uint2*>(dK + o) = wk;
+    *reinterpret_cast<uint2*>(dV + o) = wv;
   }
 }
 
@@ -446,11 +499,12 @@ static int stream_grid(size_t n4) {
 hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dO, void* dQ, void* dK,
                       void* dV, const BwdItem* items_dev, int n_items, const FwdItem* qitems_dev,
-                      int n_qitems, float* delta, float* dk_acc, float* dv_acc,
-                      hipStream_t stream, int phase_mask) {
+                      int n_qitems, float* delta, float* dk_acc, float* dv_acc, float* part,
+                      const int* tile_off, const int* tile_items, int n_tiles, hipStream_t stream,
+                      int phase_mask) {
   const size_t nk = (size_t)pb.T * pb.Hkv * pb.d;
   const float c = pb.scale * kLog2e;
-  // 1. D and zeroed dK / dV accumulators
+  // 1. D and (atomic mode) zeroed dK / dV accumulators
   if (phase_mask & 1) {
     const long long lanes = (long long)pb.T * pb.Hq * (pb.d / 8);
     dim3 grid((unsigned)((lanes + 255) / 256));
@@ -460,23 +514,26 @@ hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const voi
     else
       hipLaunchKernelGGL(pre_kernel<64>, grid, dim3(256), 0, stream, (const u16*)o,
                          (const u16*)dO, delta, pb.T, pb.Hq);
-    hipLaunchKernelGGL(zero_kernel, dim3(stream_grid(nk / 4)), dim3(256), 0, stream,
-                       (float4*)dk_acc, nk / 4);
-    hipLaunchKernelGGL(zero_kernel, dim3(stream_grid(nk / 4)), dim3(256), 0, stream,
-                       (float4*)dv_acc, nk / 4);
+    if (!part) {
+      hipLaunchKernelGGL(zero_kernel, dim3(stream_grid(nk / 4)), dim3(256), 0, stream,
+                         (float4*)dk_acc, nk / 4);
+      hipLaunchKernelGGL(zero_kernel, dim3(stream_grid(nk / 4)), dim3(256), 0, stream,
+                         (float4*)dv_acc, nk / 4);
+    }
   }
-  // 2. dK / dV (key-stationary)
+  // 2. dK / dV (key-stationary): atomics into the accumulators, or (part != null)
+  //    per-item partials
   if ((phase_mask & 2) && n_items > 0) {
     HeadMap hm = make_headmap(n_items, pb.Hkv);
     dim3 grid(headmap_grid(hm)), block(64 * kBwdWaves);
     if (pb.d == 128)
       hipLaunchKernelGGL((dkv_kernel<128>), grid, block, 0, stream, (const u16*)q,
                          (const u16*)k, (const u16*)v, (const u16*)dO, lse, delta, dk_acc, dv_acc,
-                         items_dev, hm, pb.T, pb.Hq, pb.Hkv, c);
+                         part, items_dev, hm, pb.T, pb.Hq, pb.Hkv, c);
     else
       hipLaunchKernelGGL((dkv_kernel<64>), grid, block, 0, stream, (const u16*)q,
                          (const u16*)k, (const u16*)v, (const u16*)dO, lse, delta, dk_acc, dv_acc,
-                         items_dev, hm, pb.T, pb.Hq, pb.Hkv, c);
+                         part, items_dev, hm, pb.T, pb.Hq, pb.Hkv, c);
   }
   // 8. dQ (query-stationary), written directly as bf16
   if ((phase_mask & 8) && n_qitems > 0) {
@@ -491,12 +548,24 @@ hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const voi
                          (const u16*)v, (const u16*)dO, lse, delta, (u16*)dQ, qitems_dev, hm, pb.T,
                          pb.Hq, pb.Hkv, c, pb.scale);
   }
-  // 3. dK, dV to bf16
+  // 4. dK, dV to bf16: convert the accumulators, or reduce the partials in order
   if (phase_mask & 4) {
-    hipLaunchKernelGGL(convert_kernel, dim3(stream_grid(nk / 4)), dim3(256), 0, stream,
-                       (const float4*)dk_acc, (uint2*)dK, nk / 4, pb.scale);
-    hipLaunchKernelGGL(convert_kernel, dim3(stream_grid(nk / 4)), dim3(256), 0, stream,
-                       (const float4*)dv_acc, (uint2*)dV, nk / 4, 1.0f);
+    if (part) {
+      if (n_tiles > 0) {
+        dim3 grid((unsigned)(n_tiles * pb.Hkv));
+        if (pb.d == 128)
+          hipLaunchKernelGGL(reduce_kernel<128>, grid, dim3(256), 0, stream, part, items_dev,
+                             tile_off, tile_items, (u16*)dK, (u16*)dV, pb.Hkv, pb.scale);
+        else
+          hipLaunchKernelGGL(reduce_kernel<64>, grid, dim3(256), 0, stream, part, items_dev,
+                             tile_off, tile_items, (u16*)dK, (u16*)dV, pb.Hkv, pb.scale);
+      }
+    } else {
+      hipLaunchKernelGGL(convert_kernel, dim3(stream_grid(nk / 4)), dim3(256), 0, stream,
+                         (const float4*)dk_acc, (uint2*)dK, nk / 4, pb.scale);
+      hipLaunchKernelGGL(convert_kernel, dim3(stream_grid(nk / 4)), dim3(256), 0, stream,
+                         (const float4*)dv_acc, (uint2*)dV, nk / 4, 1.0f);
+    }
   }
   return hipGetLastError();
 }

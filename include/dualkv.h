@@ -70,8 +70,10 @@ size_t dualkv_fwd_workspace_bytes(int P, int R, int N, const int32_t* offsets,
                                   int Hq, int Hkv, int d);
 
 /* Workspace dualkv_bwd needs: the two work lists, D = rowsum(dO*O) [Hq][T]
- * fp32, and fp32 accumulators for dK and dV [T][Hkv][d] (dQ is written
- * directly). 0 if the arguments are invalid. */
+ * fp32, and either fp32 accumulators for dK and dV [T][Hkv][d] (atomic mode)
+ * or, with deterministic != 0, per-work-item dK/dV partials plus the lists of
+ * each key tile's items (dQ is written directly in both modes). 0 if the
+ * arguments are invalid. */
 size_t dualkv_bwd_workspace_bytes(int P, int R, int N, const int32_t* offsets,
                                   int Hq, int Hkv, int d, int deterministic);
 
@@ -86,8 +88,10 @@ dualkv_status dualkv_fwd(const void* q, const void* k, const void* v, void* o, f
 /* Backward pass of L = sum_t <dO_t, O_t> (p1 "Approach": gradients of the
  * shared prompt accumulated across all N sequences with fp32 atomics).
  * Reads q, k, v, o, lse (from dualkv_fwd on the same inputs) and dO; writes
- * dQ, dK, dV (bf16). deterministic must be 0: the reproducible-order
- * reduction mode is not built and returns DUALKV_ERR_UNSUPPORTED. */
+ * dQ, dK, dV (bf16). deterministic = 0 adds the row-chunk partials of dK and
+ * dV with fp32 atomics (last bits depend on their order); deterministic != 0
+ * stores the partials and sums them in a fixed order, so repeated calls on the
+ * same inputs are bitwise identical (larger workspace, see above). */
 dualkv_status dualkv_bwd(const void* q, const void* k, const void* v, const void* o,
                          const float* lse, const void* dO, void* dQ, void* dK, void* dV,
                          int P, int R, int N, const int32_t* offsets,
@@ -95,11 +99,12 @@ dualkv_status dualkv_bwd(const void* q, const void* k, const void* v, const void
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* The backward of dualkv_bwd split into its stream-ordered phases, so a
- * caller can time or interleave them: bit 1 = preprocess (D = rowsum(dO*O),
- * zeroed fp32 dK, dV accumulators in the workspace), bit 2 = key-stationary
- * dK, dV pass (two KV regions, fp32 atomics into the accumulators), bit 8 =
- * query-stationary dQ pass (writes dQ), bit 4 = finish (accumulators -> bf16
- * dK, dV). Same arguments and checks as dualkv_bwd, which is phase_mask 15.
+ * caller can time or interleave them: bit 1 = preprocess (D = rowsum(dO*O);
+ * in atomic mode also zeroed fp32 dK, dV accumulators), bit 2 = key-stationary
+ * dK, dV pass (two KV regions; atomics into the accumulators, or partials in
+ * deterministic mode), bit 8 = query-stationary dQ pass (writes dQ), bit 4 =
+ * finish (accumulators -> bf16 dK, dV, or the ordered reduction of the
+ * partials). Same arguments and checks as dualkv_bwd, which is phase_mask 15.
  * Bit 1 must run before bits 2, 4 and 8, and bit 2 before bit 4, on the same
  * workspace with the same arguments; a mask of 0 or above 15 is
  * DUALKV_ERR_INVALID_ARG. */

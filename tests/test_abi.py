@@ -92,7 +92,7 @@ def test_fwd_rejects_bad_arguments(lib, kw, status):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(det=1), ERR_UNSUPPORTED),
+    (dict(det=1, ws_bytes=16), ERR_WORKSPACE),
     (dict(N=0), ERR_INVALID_ARG),
     (dict(Hq=3, Hkv=2), ERR_INVALID_ARG),
     (dict(d=32), ERR_UNSUPPORTED),
@@ -123,8 +123,9 @@ def test_workspace_sizes(lib):
     # bwd holds at least D [Hq,T] and fp32 dK/dV accumulators (dQ is written directly)
     assert nb >= 4 * (4 * T + 2 * T * 2 * 64)
     assert nb < 4 * (4 * T + 2 * T * 2 * 64) + 4 * T * 4 * 64
-    with pytest.raises(binding.DualKVError):
-        binding.bwd_workspace_bytes(pk, 4, 2, 64, deterministic=True)
+    # deterministic mode holds per-item dK/dV partials instead of the accumulators
+    nd = binding.bwd_workspace_bytes(pk, 4, 2, 64, deterministic=True)
+    assert nd > 0 and nd % 256 == 0 and nd != nb
     with pytest.raises(binding.DualKVError):
         binding.fwd_workspace_bytes(pk, 4, 3, 64)
     # ragged offsets are accepted and size like the uniform case of equal T

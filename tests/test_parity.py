@@ -37,12 +37,12 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_gpu(inp):
+def run_gpu(inp, deterministic=False):
     dev = torch.device("cuda:0")
     q, k, v, do = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.do))
     pk = binding.Packing(inp.P, inp.lengths)
     o, lse = binding.fwd(q, k, v, pk, inp.scale)
-    dq, dk, dv = binding.bwd(q, k, v, o, lse, do, pk, inp.scale)
+    dq, dk, dv = binding.bwd(q, k, v, o, lse, do, pk, inp.scale, deterministic=deterministic)
     torch.cuda.synchronize()
     out = {"O": o, "LSE": lse, "dQ": dq, "dK": dk, "dV": dv}
     res = {kk: t.float().cpu().numpy() for kk, t in out.items()}
@@ -144,6 +144,35 @@ def test_repeat_calls_agree_within_tolerance():
         assert np.array_equal(a[key], b[key]), key
     for key in ("dQ", "dK", "dV"):
         assert rel(a[key], b[key]) <= 1e-3, key
+
+
+@pytest.mark.parametrize("name", ["ragged_tails_p300", "ragged_d64_many", "gqa8_p192"])
+def test_deterministic_mode_parity_and_bitwise_repeat(name):
+    """Deterministic mode: same bar against the oracle, and two calls give
+    bitwise-identical dQ, dK, dV."""
+    kw = dict(SMALL[name])
+    P, lengths, Hq, Hkv, d, seed = (kw.pop(x) for x in ("P", "lengths", "Hq", "Hkv", "d", "seed"))
+    inp = make_inputs(P, lengths, Hq, Hkv, d, seed=seed, **kw)
+    say(f"case deterministic {name}: P={P} lengths={lengths} Hq={Hq} Hkv={Hkv} d={d}")
+    a = run_gpu(inp, deterministic=True)
+    b = run_gpu(inp, deterministic=True)
+    for key in ("O", "LSE", "dQ", "dK", "dV"):
+        assert np.array_equal(a[key], b[key]), key
+    ref = oracle_fwd_bwd(np64(inp.q), np64(inp.k), np64(inp.v), np64(inp.do), P, lengths, inp.scale)
+    check_all(a, ref, P, name + " det")
+
+
+def test_deterministic_mode_bitwise_repeat_multi_chunk():
+    """Long enough that prompt tiles span several row chunks (so the ordered
+    reduction sums many partials); the atomic result agrees to fp32 rounding."""
+    inp = make_inputs(4096, [2500, 3000, 1800], 8, 2, 128, seed=34)
+    say("case deterministic multi-chunk: P=4096 lengths=[2500, 3000, 1800]")
+    a = run_gpu(inp, deterministic=True)
+    b = run_gpu(inp, deterministic=True)
+    c = run_gpu(inp, deterministic=False)
+    for key in ("dQ", "dK", "dV"):
+        assert np.array_equal(a[key], b[key]), key
+        assert rel(a[key], c[key]) <= 1e-3, key
 
 
 # ----------------------------------------------------------- full sizes --
