@@ -50,7 +50,9 @@ dualkv_status check_shape(int P, int R, int N, const int32_t* offsets, int Hq, i
     T = (long long)P + (long long)N * R;
   }
   if (T >= (1LL << 31)) return DUALKV_ERR_INVALID_ARG;
-  if (T * (long long)std::max(Hq, Hkv) * d >= (1LL << 31)) return DUALKV_ERR_INVALID_ARG;
+  // element offsets are 64-bit everywhere; this bound keeps every launch grid
+  // (one lane per 8 elements in the preprocess) well inside 32 bits
+  if (T * (long long)std::max(Hq, Hkv) * d >= (1LL << 40)) return DUALKV_ERR_INVALID_ARG;
   pb.P = P;
   pb.N = N;
   pb.R = offsets ? 0 : R;

@@ -157,7 +157,90 @@ __global__ __launch_bounds__(256) void atomic_kernel(float* buf, int rows, int i
   }
 }
 
+// VALU issue rate: 8 independent chains per lane of one operation, `iters`
+// rounds. op 0: v_exp_f32 (transcendental unit), 1: v_fma_f32, 2: v_cvt_pk_bf16_f32.
+template <int OP>
+__global__ __launch_bounds__(256) void valu_rate_kernel(float* out, int iters, float seed) {
+  float x[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) x[u] = seed * (float)(threadIdx.x + u) - 0.5f;
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (OP == 0) x[u] = __builtin_amdgcn_exp2f(-x[u]);
+      else if (OP == 1) x[u] = fmaf(x[u], 0.999f, seed);
+      else {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        f32x2 f = {x[u], x[(u + 1) & 7]};
+        x[u] = __builtin_bit_cast(float, __builtin_convertvector(f, bf16x2));
+      }
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) s += x[u];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+// MFMA and exp in one wave: per round four independent 32x32x16 MFMAs (if MF)
+// and NEXP independent exp2 per lane (8 chains).
+template <bool MF, int NEXP>
+__global__ __launch_bounds__(256) void mix_kernel(float* out, int iters, float seed) {
+  bf16x8 a, b;
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(seed * (float)(threadIdx.x + e));
+    b[e] = (__bf16)(seed * (float)(e - (int)threadIdx.x));
+  }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  float x[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) x[u] = seed * (float)(threadIdx.x + u) + 0.25f;
+  for (int i = 0; i < iters; ++i) {
+    if (MF) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < NEXP; j += 8)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = __builtin_amdgcn_exp2f(-x[u]);
+  }
+  float s = 0.f;
+  for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) s += x[u];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 extern "C" {
+
+// VALU rate: blocks x 256 threads x iters x 8 operations of kind op (0 exp2,
+// 1 fma, 2 cvt_pk_bf16).
+int dkv_mb_valu(int op, int blocks, int iters, float* out, void* stream) {
+  if (op == 0)
+    hipLaunchKernelGGL(valu_rate_kernel<0>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters, 1e-3f);
+  else if (op == 1)
+    hipLaunchKernelGGL(valu_rate_kernel<1>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters, 1e-3f);
+  else if (op == 2)
+    hipLaunchKernelGGL(valu_rate_kernel<2>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters, 1e-3f);
+  else
+    return (int)hipErrorInvalidValue;
+  return (int)hipGetLastError();
+}
+
+// MFMA / exp overlap: see mix_kernel. (do_mfma, nexp): (1, 0), or nexp in {16, 32, 64}.
+int dkv_mb_mix(int blocks, int iters, int do_mfma, int nexp, float* out, void* stream) {
+  const dim3 g(blocks), b(256);
+  hipStream_t st = (hipStream_t)stream;
+#define DKV_MIX(MF, NE) \
+  if (do_mfma == MF && nexp == NE) { hipLaunchKernelGGL((mix_kernel<MF, NE>), g, b, 0, st, out, iters, 1e-3f); return (int)hipGetLastError(); }
+  DKV_MIX(1, 0) DKV_MIX(0, 16) DKV_MIX(1, 16) DKV_MIX(0, 32) DKV_MIX(1, 32) DKV_MIX(0, 64) DKV_MIX(1, 64)
+#undef DKV_MIX
+  return (int)hipErrorInvalidValue;
+}
 
 // blocks x 256 threads x iters x 16 atomic lanes into buf[rows * 128] (rows >= 64).
 int dkv_mb_atomic(int blocks, int iters, float* buf, int rows, void* stream) {

@@ -31,6 +31,11 @@ def _load():
             fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
         _lib.dkv_mb_atomic.restype = ctypes.c_int
         _lib.dkv_mb_atomic.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+        _lib.dkv_mb_valu.restype = ctypes.c_int
+        _lib.dkv_mb_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        _lib.dkv_mb_mix.restype = ctypes.c_int
+        _lib.dkv_mb_mix.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.c_void_p]
         _lib.dkv_mb_copy.restype = ctypes.c_int
         _lib.dkv_mb_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p]
     return _lib
@@ -123,6 +128,35 @@ def lds_bytes_per_clk(iters: int = 4096) -> dict:
         sec = _time(lib.dkv_mb_lds_b128_deep, blocks, iters)
         total = blocks * 256 * iters * 8 * 16
         res[f"b128_deep_{4 * wg_per_cu}waves"] = total / sec / cu_count() / clock_hz()
+    return res
+
+
+def valu_cycles_per_instruction(iters: int = 8192) -> dict:
+    """SIMD cycles per wave64 instruction for exp2, fma and cvt_pk_bf16, at
+    4 and 8 waves per CU, from the measured time and the reported clock."""
+    lib = _load()
+    res = {}
+    for wg in (1, 2):
+        blocks = cu_count() * wg
+        for op, name in ((0, "exp2"), (1, "fma"), (2, "cvt_pk_bf16")):
+            sec = _time(lambda b, it, o, s: lib.dkv_mb_valu(op, b, it, o, s), blocks, iters)
+            insts_per_simd = blocks * 4 * iters * 8 / (cu_count() * 4)
+            res[f"{name}_{4 * wg}waves"] = sec * clock_hz() / insts_per_simd
+    return res
+
+
+def mfma_exp_overlap(iters: int = 4096) -> dict:
+    """Time per round (4 MFMAs and/or nexp exp2 per wave), in SIMD cycles per
+    wave, for MFMA alone, exp alone and both, at 4 and 8 waves per CU."""
+    lib = _load()
+    res = {}
+    for wg in (1, 2):
+        blocks = cu_count() * wg
+        for nexp in (16, 32, 64):
+            for mf, tag in ((1, "mfma"), (0, "exp"), (1, "both")):
+                ne = 0 if tag == "mfma" else nexp
+                sec = _time(lambda b, it, o, s: lib.dkv_mb_mix(b, it, mf, ne, o, s), blocks, iters)
+                res[f"{4 * wg}w_nexp{nexp}_{tag}"] = sec * clock_hz() / (iters * wg)
     return res
 
 

@@ -27,7 +27,7 @@
  *    offsets non-decreasing and offsets[N] == T (R is ignored). Empty
  *    responses (R_n = 0) and P == 0 (the replicated, unshared layout) are
  *    allowed.
- *  - Supported head_dim d: 64, 128. T * max(Hq, Hkv) * d must stay below 2^31.
+ *  - Supported head_dim d: 64, 128. T < 2^31 and T * max(Hq, Hkv) * d < 2^40.
  *  - Ownership: the caller owns every device buffer, including the
  *    workspace; the library allocates no device memory. Its only state is a
  *    small ring of pinned host staging buffers (grown on demand, kept for the

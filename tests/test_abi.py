@@ -83,7 +83,7 @@ def _bwd(lib, P=16, R=8, N=2, Hq=4, Hkv=2, d=128, scale=0.1, det=0, ws=FAKE, ws_
     (dict(offsets=[15, 20, 30], N=2), ERR_INVALID_ARG),  # offsets[0] != P
     (dict(offsets=[16, 30, 20], N=2), ERR_INVALID_ARG),  # decreasing
     (dict(R=1 << 12, N=1 << 20), ERR_INVALID_ARG),  # T >= 2^31
-    (dict(P=1 << 22, Hq=32, Hkv=8, d=128, R=0), ERR_INVALID_ARG),  # T*Hq*d >= 2^31
+    (dict(P=1 << 30, Hq=64, Hkv=8, d=128, R=0), ERR_INVALID_ARG),  # T*Hq*d >= 2^40
     (dict(ws=None), ERR_WORKSPACE),
     (dict(ws_bytes=1), ERR_WORKSPACE),
 ])

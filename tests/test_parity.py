@@ -248,3 +248,35 @@ def test_full_size_sampled(name):
         sv = got["dV"][:, g].astype(np.float64).sum(0)
         want = do[:, g * G:(g + 1) * G].astype(np.float64).sum((0, 1))
         assert rel(sv, want) <= REL, ("sum dV", g)
+
+
+def test_tensors_beyond_2_31_elements_sampled():
+    """Q, O, dO, dQ with more than 2^31 elements (64 query heads, 262656
+    tokens: 1025 responses of 256 after a 256-token prompt). Rows and keys
+    whose element offsets lie past 2^31 are checked against the oracle."""
+    P, N, R, Hq, Hkv, d = 256, 1025, 256, 64, 8, 128
+    L = [R] * N
+    T = P + N * R
+    assert T * Hq * d > 2 ** 31
+    say(f"case beyond 2^31: generating inputs T={T} Hq={Hq}")
+    inp = make_inputs(P, L, Hq, Hkv, d, seed=71)
+    say("case beyond 2^31: running fwd+bwd on the GPU")
+    got = run_gpu(inp)
+    first_past = (2 ** 31) // (Hq * d)   # first row whose elements start past 2^31
+    rows = sorted({0, P - 1, P, T // 2, first_past - 1, first_past, first_past + 77, T - R, T - 2, T - 1})
+    q, k, v, do = (t.float().numpy() for t in (inp.q, inp.k, inp.v, inp.do))
+    say(f"case beyond 2^31: oracle on rows {rows}")
+    ref = rows_fwd_bwd(q, k, v, do, P, L, inp.scale, rows)
+    for key in ("O", "dQ"):
+        e = rel(got[key][rows], ref[key])
+        say(f"  rows {key}: rel {e:.2e}")
+        assert e <= REL, key
+    assert float(np.max(np.abs(got["LSE"][:, rows] - ref["LSE"]))) <= LSE_ABS
+    keys = list(range(T - R, T - R + 8)) + list(range(T - 8, T))   # last response: its rows lie past 2^31
+    for g in (0, Hkv - 1):
+        rk = keys_dkdv(q, k, v, do, P, L, inp.scale, keys, g)
+        for key in ("dK", "dV"):
+            e = rel(got[key][keys, g], rk[key])
+            say(f"  last-response {key} g={g}: rel {e:.2e}")
+            assert e <= REL, (key, g)
+
