@@ -15,8 +15,10 @@
 #include "common.h"
 
 namespace dkv {
-hipError_t launch_fwd(const Problem& pb, const void* q, const void* k, const void* v, void* o,
+hipError_t launch_fwd(const Problem& pb, const void* q, const void* k, const void* vt, void* o,
                       float* lse, const FwdItem* items_dev, int n_items, hipStream_t stream);
+hipError_t launch_xpose_kv(const Problem& pb, const void* src, void* dst, const KeyBlock* blocks_dev,
+                           int n_blocks, hipStream_t stream);
 hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dO, void* dQ, void* dK,
                       void* dV, const BwdItem* items_dev, int n_items, const FwdItem* qitems_dev,
@@ -53,6 +55,8 @@ dualkv_status check_shape(int P, int R, int N, const int32_t* offsets, int Hq, i
   // element offsets are 64-bit everywhere; this bound keeps every launch grid
   // (one lane per 8 elements in the preprocess) well inside 32 bits
   if (T * (long long)std::max(Hq, Hkv) * d >= (1LL << 40)) return DUALKV_ERR_INVALID_ARG;
+  // per-lane copy offsets within a 64-key tile are 32-bit
+  if ((long long)Hkv * d >= (1LL << 20)) return DUALKV_ERR_INVALID_ARG;
   pb.P = P;
   pb.N = N;
   pb.R = offsets ? 0 : R;
@@ -120,17 +124,33 @@ hipError_t upload(void* dst, const void* src, size_t n, hipStream_t stream) {
   return staging->upload(dst, src, n, stream);
 }
 
+// 32-key blocks of the transposed K / V fragments, cut per region (the
+// prompt, then each response); base[n] = first block of response n.
+std::vector<KeyBlock> key_blocks(const Problem& pb, std::vector<int>* base = nullptr) {
+  std::vector<KeyBlock> blocks;
+  for (int kb = 0; kb < pb.P; kb += 32) blocks.push_back({kb, pb.P});
+  if (base) base->clear();
+  for (int n = 0; n < pb.N; ++n) {
+    const int a = pb.seg_start(n), b = pb.seg_start(n + 1);
+    if (base) base->push_back((int)blocks.size());
+    for (int kb = a; kb < b; kb += 32) blocks.push_back({kb, b});
+  }
+  return blocks;
+}
+
 // Forward (and dQ) work list: query tiles of `rows` rows that never straddle
 // a segment, longest (most keys) first so the tail of the grid is short.
 std::vector<FwdItem> fwd_items(const Problem& pb, int rows = kFwdRows) {
+  std::vector<int> base;
+  key_blocks(pb, &base);
   std::vector<FwdItem> items;
   for (int r = 0; r < pb.P; r += rows) {
     const int r1 = std::min(pb.P, r + rows);
-    items.push_back({r, r1, r1, r1});
+    items.push_back({r, r1, r1, r1, 0});
   }
   for (int n = 0; n < pb.N; ++n) {
     const int a = pb.seg_start(n), b = pb.seg_start(n + 1);
-    for (int r = a; r < b; r += rows) items.push_back({r, std::min(b, r + rows), pb.P, a});
+    for (int r = a; r < b; r += rows) items.push_back({r, std::min(b, r + rows), pb.P, a, base[n]});
   }
   std::stable_sort(items.begin(), items.end(), [](const FwdItem& x, const FwdItem& y) {
     return (x.a_end + x.r1 - x.b_start) > (y.a_end + y.r1 - y.b_start);
@@ -177,6 +197,21 @@ std::vector<BwdItem> bwd_items(const Problem& pb, TileLists* tl_out = nullptr) {
   return items;
 }
 
+// Forward workspace: work list, key blocks, V^T fragments
+// [block][Hkv][d/32][2][64][8] bf16.
+struct FwdLayout {
+  size_t items, blocks, vt, total;
+};
+FwdLayout fwd_layout(const Problem& pb, size_t n_items, size_t n_blocks) {
+  FwdLayout L{};
+  size_t off = 0;
+  L.items = off;  off = align_up(off + std::max<size_t>(1, n_items) * sizeof(FwdItem));
+  L.blocks = off; off = align_up(off + std::max<size_t>(1, n_blocks) * sizeof(KeyBlock));
+  L.vt = off;     off = align_up(off + n_blocks * pb.Hkv * (size_t)pb.d * 32 * sizeof(uint16_t));
+  L.total = off;
+  return L;
+}
+
 struct BwdLayout {
   size_t items, qitems, delta, dk, dv, part, tile_off, tile_items, total;
 };
@@ -210,7 +245,7 @@ size_t dualkv_fwd_workspace_bytes(int P, int R, int N, const int32_t* offsets, i
                                   int d) {
   Problem pb;
   if (check_shape(P, R, N, offsets, Hq, Hkv, d, pb) != DUALKV_OK) return 0;
-  return align_up(std::max<size_t>(1, fwd_items(pb).size()) * sizeof(FwdItem));
+  return fwd_layout(pb, fwd_items(pb).size(), key_blocks(pb).size()).total;
 }
 
 size_t dualkv_bwd_workspace_bytes(int P, int R, int N, const int32_t* offsets, int Hq, int Hkv,
@@ -235,15 +270,20 @@ dualkv_status dualkv_fwd(const void* q, const void* k, const void* v, void* o, f
     return DUALKV_ERR_INVALID_ARG;
   pb.scale = softmax_scale;
   const std::vector<FwdItem> items = fwd_items(pb);
-  const size_t need = align_up(std::max<size_t>(1, items.size()) * sizeof(FwdItem));
-  if (!workspace || workspace_bytes < need) return DUALKV_ERR_WORKSPACE;
+  const std::vector<KeyBlock> blocks = key_blocks(pb);
+  const FwdLayout L = fwd_layout(pb, items.size(), blocks.size());
+  if (!workspace || workspace_bytes < L.total) return DUALKV_ERR_WORKSPACE;
   if (!aligned16(workspace)) return DUALKV_ERR_INVALID_ARG;
   if (items.empty()) return DUALKV_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (upload(workspace, items.data(), items.size() * sizeof(FwdItem), s) != hipSuccess)
+  char* ws = static_cast<char*>(workspace);
+  if (upload(ws + L.items, items.data(), items.size() * sizeof(FwdItem), s) != hipSuccess ||
+      upload(ws + L.blocks, blocks.data(), blocks.size() * sizeof(KeyBlock), s) != hipSuccess)
     return DUALKV_ERR_HIP;
-  if (launch_fwd(pb, q, k, v, o, lse, static_cast<const FwdItem*>(workspace), (int)items.size(),
-                 s) != hipSuccess)
+  if (launch_xpose_kv(pb, v, ws + L.vt, reinterpret_cast<const KeyBlock*>(ws + L.blocks),
+                      (int)blocks.size(), s) != hipSuccess ||
+      launch_fwd(pb, q, k, ws + L.vt, o, lse, reinterpret_cast<const FwdItem*>(ws + L.items),
+                 (int)items.size(), s) != hipSuccess)
     return DUALKV_ERR_HIP;
   return DUALKV_OK;
 }

@@ -34,7 +34,14 @@ struct Problem {
 // Forward work item: query rows [r0, r1) of one segment; KV region A is
 // [0, a_end) (the prompt, or the prompt rows up to r1 for a prompt tile) and
 // region B is [b_start, r1) (the own response; empty for a prompt tile).
-struct FwdItem { int r0, r1, a_end, b_start; };
+// b_blk is the index of region B's first 32-key block in the transposed
+// fragment layout (blocks are cut per region: the prompt's, then each
+// response's, so a region's tiles start on a block).
+struct FwdItem { int r0, r1, a_end, b_start, b_blk; };
+
+// 32-key block of the transposed fragment layout: keys [key0, key0 + 32)
+// clamped to [key0, kend) (kend = end of the block's region).
+struct KeyBlock { int key0, kend; };
 
 // Backward work item: keys [kb, ke) of one KV tile, query rows [r0, r1).
 // Every row in [r0, r1) with row >= key attends the key (prompt keys are seen

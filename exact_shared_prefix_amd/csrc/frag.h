@@ -30,6 +30,13 @@ __device__ __forceinline__ void dma16(const void* g, void* lds_base) {
   const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory", "m0");
 }
+// Same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte
+// offset (no per-lane 64-bit address arithmetic).
+__device__ __forceinline__ void dma16s(const void* base, uint32_t voff, void* lds_base) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(m)
+               : "memory", "m0");
+}
 __device__ __forceinline__ void dma4(const void* g, void* lds_base) {
   const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m) : "memory", "m0");

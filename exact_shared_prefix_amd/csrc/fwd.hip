@@ -6,15 +6,17 @@
 //
 // gfx950 design:
 //  * one workgroup = 8 waves x 32 query rows = 256 rows of one query head, all
-//    in one segment (the prompt or one response); two waves per SIMD;
+//    in one segment (the prompt or one response);
 //  * S^T = K Q^T on bf16 MFMA 32x32x16 with Q in registers: a lane owns one
 //    query column, so the row max / row sum are lane-local plus one swap
 //    between the wave halves;
 //  * O^T += V^T P^T takes P^T straight from the S^T accumulator as its B
-//    operand; the V^T A fragments are made once per tile by MFMA transposes
-//    (one 32 x 32 block per wave);
-//  * 64-key K and V tiles arrive by direct global -> LDS copies one tile ahead,
-//    as fragment-native A operands (lane-linear 16-byte LDS accesses only);
+//    operand; the V^T A fragments are made once per call by a transpose pass
+//    over V (xpose_kv_kernel) and copied like K;
+//  * 64-key K and V^T tiles arrive by direct global -> LDS copies two steps
+//    ahead, as fragment-native A operands (lane-linear 16-byte LDS reads);
+//  * the two waves of a SIMD run one phase apart, so one issues its matrix
+//    products while the other computes its softmax;
 //  * scores are kept in the log2 domain (scale * log2 e folded in), exp2 on the
 //    transcendental unit; the running max moves only when a row's max grows
 //    by more than 2^8, so the O rescale is skipped in almost every tile; LSE
@@ -24,23 +26,63 @@
 
 namespace dkv {
 
+// Transposed fragments of K or V: for every 32-key block b of the per-region
+// block list and KV head g, the A operands X^T[d][key] of the 2 * D / 32
+// (d tile, 16-key step) pairs, in the k-slot order of a P^T (dS^T) B operand:
+// lane l = 32 hl + i holds d = 32 dt + i and, in slot e, key
+// key0 + 16 ks + 8 (e / 4) + 4 hl + e % 4 (keys past the region end repeat
+// its last key). Layout [block][g][dt][ks][64 lanes][8].
 template <int D>
+__global__ __launch_bounds__(256) void xpose_kv_kernel(const u16* __restrict__ src,
+                                                       u16* __restrict__ dst,
+                                                       const KeyBlock* __restrict__ blocks, int Hkv) {
+  constexpr int NF = 2 * (D / 32);
+  constexpr int LD = D + 8;   // padded LDS row (elements)
+  __shared__ __attribute__((aligned(16))) u16 tile[32 * LD];
+  const int b = blockIdx.x, g = blockIdx.y;
+  const KeyBlock kb = blocks[b];
+  const size_t krow = (size_t)Hkv * D;
+  for (int x = threadIdx.x; x < 32 * (D / 8); x += 256) {
+    const int r = x / (D / 8), c = x % (D / 8);
+    const int key = min(kb.key0 + r, kb.kend - 1);
+    *reinterpret_cast<uint4*>(tile + r * LD + 8 * c) =
+        *reinterpret_cast<const uint4*>(src + (size_t)key * krow + (size_t)g * D + 8 * c);
+  }
+  __syncthreads();
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, hl = lane >> 5, i = lane & 31;
+  for (int f = wv; f < NF; f += 4) {
+    const int dt = f >> 1, ks = f & 1;
+    u16 e8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) e8[e] = tile[(16 * ks + 8 * (e >> 2) + 4 * hl + (e & 3)) * LD + 32 * dt + i];
+    uint4 w4;
+    w4.x = e8[0] | ((uint32_t)e8[1] << 16);
+    w4.y = e8[2] | ((uint32_t)e8[3] << 16);
+    w4.z = e8[4] | ((uint32_t)e8[5] << 16);
+    w4.w = e8[6] | ((uint32_t)e8[7] << 16);
+    *reinterpret_cast<uint4*>(dst + (((size_t)b * Hkv + g) * NF + f) * kFrag + 8 * lane) = w4;
+  }
+}
+
+// ZERO_SCALE: the softmax scale is 0, so a masked score (-inf) times the scale
+// is not -inf and masked probabilities are zeroed explicitly
+template <int D, bool ZERO_SCALE>
 __global__ __launch_bounds__(64 * kFwdWaves, 1) void fwd_kernel(
-    const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
+    const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ vt,
     u16* __restrict__ o, float* __restrict__ lse, const FwdItem* __restrict__ items,
     HeadMap hm, int T, int Hq, int Hkv, float c /* softmax scale * log2(e) */) {
   constexpr int NW = kFwdWaves;
   constexpr int BK = 64;          // keys per tile
   constexpr int NKK = D / 16;
   constexpr int NDT = D / 32;
-  constexpr int NTF = 2 * NKK;    // K (or V) fragments per tile: 2 key blocks x NKK
-  constexpr int NJOB = 2 * NTF;   // copies per tile (K and V)
-  static_assert(NJOB % NW == 0 && 2 * NDT <= NW, "copies and transposes per wave");
+  constexpr int NTF = 2 * NKK;    // K (or V^T) fragments per tile
+  constexpr int NL = NW / 2;      // leading waves; the other NL waves issue the copies
+  constexpr int NC = NTF / NL;    // copies of each tensor per trailing wave and tile
+  static_assert(NW == 8 && NTF % NL == 0, "copies per wave");
   __shared__ __attribute__((aligned(16))) u16 KA0[NTF * kFrag];
   __shared__ __attribute__((aligned(16))) u16 KA1[NTF * kFrag];
-  __shared__ __attribute__((aligned(16))) u16 VA0[NTF * kFrag];
-  __shared__ __attribute__((aligned(16))) u16 VA1[NTF * kFrag];
-  __shared__ __attribute__((aligned(16))) u16 VT[2 * NDT * 2 * kFrag];   // V^T A fragments [kb2][dt][ks]
+  __shared__ __attribute__((aligned(16))) u16 VT0[NTF * kFrag];   // V^T A fragments [kb2][dt][ks]
+  __shared__ __attribute__((aligned(16))) u16 VT1[NTF * kFrag];
 
   int item_id, h;
   if (!headmap_decode(hm, blockIdx.x, item_id, h)) return;
@@ -49,10 +91,13 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void fwd_kernel(
   const int g = h / G;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept in a scalar register
+  // Waves w and w + 4 share a SIMD and run the same step sequence one phase
+  // apart (the trailing wave passes one extra barrier first): while one runs
+  // its matrix products the other runs its softmax.
+  const bool lead = w < NL;
   const int hl = lane >> 5, l32 = lane & 31;
   const int t0 = it.r0 + 32 * w;   // first query row of this wave
   const int t = t0 + l32;          // this lane's query row
-  const bool wave_rows = t0 < it.r1;
   const size_t qrow = (size_t)Hq * D, krow = (size_t)Hkv * D;
 
   // Q fragments: B operand of S^T = K Q^T (lane -> query column, 8 consecutive d)
@@ -76,65 +121,83 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void fwd_kernel(
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
   float m2 = -1e30f;  // running max of the log2-domain scores (reference point)
   float lsum = 0.f;   // this lane's partial row sum (its half of the keys)
+  f32x16 s[2];        // S^T of the current tile: block kb2, register r <-> key kb + 32 kb2 + 8 (r/4) + 4 hl + r%4
+  bf16x8 pf[2][2];    // P^T of the previous tile, B operands of O^T += V^T P^T
 
   const int nA = (it.a_end + BK - 1) / BK;
   const int nB = it.r1 > it.b_start ? (it.r1 - it.b_start + BK - 1) / BK : 0;
-  const int ntiles = nA + nB;
-  auto tile_bounds = [&](int i, int& kb, int& ke) {
+  const int n = nA + nB;
+  auto tile_bounds = [&](int i, int& kb, int& ke) __attribute__((always_inline)) {
     if (i < nA) { kb = i * BK; ke = it.a_end; }
     else { kb = it.b_start + (i - nA) * BK; ke = it.r1; }
   };
-  // copies of tile i: job f = w, w + NW, ...: tensor f / NTF, key block
-  // (f / NKK) % 2, d chunk f % NKK; keys past the region end read its last key
-  auto stage = [&](int i, u16* ka, u16* va) {
+  // copies of tile i by the trailing waves (copy f = (w - NL) + NL j):
+  // K: key block f / NKK, d chunk f % NKK, keys past the region end read its
+  // last key; V^T: block f / (2 NDT) of the tile (clamped to the last block
+  // the tile needs), fragment f % (2 NDT)
+  auto copy_k = [&](int i, u16* dst) __attribute__((always_inline)) {
     int kb, ke;
     tile_bounds(i, kb, ke);
+    const u16* base = k + (size_t)kb * krow + (size_t)g * D;
 #pragma unroll
-    for (int j = 0; j < NJOB / NW; ++j) {
-      const int f = w + NW * j;
-      const int kb2 = (f / NKK) % 2, kk = f % NKK;
-      const int key = min(kb + 32 * kb2 + l32, ke - 1);
-      const u16* src = (f < NTF ? k : v) + (size_t)key * krow + (size_t)g * D + 16 * kk + 8 * hl;
-      dma16(src, (f < NTF ? ka : va) + (f % NTF) * kFrag);
+    for (int j = 0; j < NC; ++j) {
+      const int f = (w - NL) + NL * j;
+      const int kb2 = f / NKK, kk = f % NKK;
+      const uint32_t row = (uint32_t)min(32 * kb2 + l32, ke - 1 - kb);
+      dma16s(base, 2u * (row * (uint32_t)krow + 16 * kk + 8 * hl), dst + f * kFrag);
     }
   };
-
-  auto tile = [&](int i, const u16* ka, const u16* va, u16* kan, u16* van) {
+  auto copy_vt = [&](int i, u16* dst) __attribute__((always_inline)) {
     int kb, ke;
     tile_bounds(i, kb, ke);
-    vm_barrier<0>();   // tile i's copies landed; every wave is done with tile i - 1
-    if (i + 1 < ntiles) stage(i + 1, kan, van);
-    // V^T A fragments of (key block, d tile) pair w: lane -> d, k-slots in
-    // accumulator key order
-    if (w < 2 * NDT) {
-      const int kb2 = w / NDT, dt = w % NDT;
-      bf16x8 f0, f1;
-      pack2(xpose_nat(frag_ld(va + (kb2 * NKK + 2 * dt) * kFrag, lane),
-                      frag_ld(va + (kb2 * NKK + 2 * dt + 1) * kFrag, lane), lane),
-            f0, f1);
-      frag_st(VT + ((kb2 * NDT + dt) * 2) * kFrag, lane, f0);
-      frag_st(VT + ((kb2 * NDT + dt) * 2 + 1) * kFrag, lane, f1);
+    const int b0 = i < nA ? kb / 32 : it.b_blk + (kb - it.b_start) / 32;
+    const int blast = b0 + (ke - 1 - kb) / 32;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const int f = (w - NL) + NL * j;
+      const int blk = min(b0 + f / (2 * NDT), blast);
+      const u16* base = vt + ((size_t)blk * Hkv + g) * (2 * NDT * kFrag);
+      dma16s(base, 2u * ((f % (2 * NDT)) * kFrag + 8 * lane), dst + f * kFrag);
     }
-    lds_barrier();
-    if (!wave_rows || kb > t0 + 31) return;   // every key of the tile lies after this wave's rows
-
-    // S^T[key][query]: block kb2, register r <-> key kb + 32 kb2 + 8 (r/4) + 4 hl + r%4
-    f32x16 s[2] = {f32x16{}, f32x16{}};
+  };
+  // products of step j: S^T of tile j, then O^T += V^T P^T of tile j - 1
+  auto mfma_part = [&](int j, const u16* ka, const u16* vt_prev) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
+    if (j < n) {
+      s[0] = f32x16{};
+      s[1] = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
+      for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) s[kb2] = mfma32(frag_ld(ka + (kb2 * NKK + kk) * kFrag, lane), qf[kk], s[kb2]);
-    pipelined_mfma<2 * NKK, 1, 4>();
-
-    // masked scores become -inf and their exp2 exact zeros
+        for (int kb2 = 0; kb2 < 2; ++kb2) s[kb2] = mfma32(frag_ld(ka + (kb2 * NKK + kk) * kFrag, lane), qf[kk], s[kb2]);
+      pipelined_mfma<2 * NKK, 1, 4>();
+    }
+    if (j > 0) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+            oacc[dt] = mfma32(frag_ld(vt_prev + ((kb2 * NDT + dt) * 2 + ks) * kFrag, lane), pf[kb2][ks], oacc[dt]);
+      pipelined_mfma<4 * NDT, 1, 4>();
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // softmax of step j: mask, running max, P^T = exp2(S^T c - m) (bf16)
+  auto valu_part = [&](int j) __attribute__((always_inline)) {
+    int kb, ke;
+    tile_bounds(j, kb, ke);
+    // masked scores become -inf and their exp2 exact zeros (also every score of
+    // a tile that lies wholly after this wave's rows)
     const bool need_mask = (kb + BK > ke) || (kb + BK - 1 > t0);
     if (need_mask) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int j = kb + 32 * kb2 + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (j >= ke || j > t) s[kb2][r] = -INFINITY;
+          const int jj = kb + 32 * kb2 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (jj >= ke || jj > t) s[kb2][r] = -INFINITY;
         }
     }
     float mx = -INFINITY;
@@ -153,39 +216,52 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void fwd_kernel(
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
     }
-    bf16x8 pf[2][2];
     float ps = 0.f;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float x = fast_exp2(fmaf(s[kb2][r], c, -m2));
-        // explicit zero: with a softmax scale of 0, -inf * c is not -inf
-        if (need_mask && s[kb2][r] == -INFINITY) x = 0.f;
+        if (ZERO_SCALE && need_mask && s[kb2][r] == -INFINITY) x = 0.f;
         s[kb2][r] = x;
         ps += x;
       }
       pack2(s[kb2], pf[kb2][0], pf[kb2][1]);
     }
     lsum += ps;
-
-    // O^T[d][q] += V^T[d][key] P^T[key][q]
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-          oacc[dt] = mfma32(frag_ld(VT + ((kb2 * NDT + dt) * 2 + ks) * kFrag, lane), pf[kb2][ks], oacc[dt]);
-    pipelined_mfma<4 * NDT, 1, 4>();
   };
 
-  // The tile loop alternates between two statically distinct buffer sets.
-  if (ntiles > 0) stage(0, KA0, VA0);
-  for (int i = 0; i < ntiles; i += 2) {
-    tile(i, KA0, VA0, KA1, VA1);
-    if (i + 1 < ntiles) tile(i + 1, KA1, VA1, KA0, VA0);
+  // Step j of a wave: phase M (products of step j) then phase S (softmax of
+  // tile j). Phase M of a leading wave coincides with phase S of step j - 1 of
+  // its trailing partner, and the other way round. The trailing waves copy
+  // K(j + 2) and V^T(j + 1) during their phase S(j) and wait for them at the
+  // barrier that ends their phase S(j + 1), which is where the leading waves
+  // start phase M(j + 2) (K(j + 2) lands in the buffer K(j) used, V^T(j + 1)
+  // in the one V^T(j - 1) used).
+  auto step = [&](int j, u16* ka, u16* vt_prev) __attribute__((always_inline)) {
+    lds_barrier();     // leading: K(j), V^T(j - 1) landed (the trailing waves waited for them)
+    mfma_part(j, ka, vt_prev);
+    vm_barrier<0>();   // trailing: copies issued in phase S(j - 1) landed
+    if (!lead) {
+      if (j + 2 < n) copy_k(j + 2, ka);
+      if (j + 1 < n) copy_vt(j + 1, vt_prev);
+    }
+    if (j < n) valu_part(j);
+  };
+
+  if (!lead) {
+    if (n > 0) copy_k(0, KA0);
+    vm_barrier<0>();
+    if (n > 1) copy_k(1, KA1);
+    if (n > 0) copy_vt(0, VT0);
   }
+  // steps 0 .. n (step n only finishes tile n - 1), two per iteration so that
+  // every buffer is a static LDS address
+  for (int j = 0; j <= n; j += 2) {
+    step(j, KA0, VT1);
+    if (j + 1 <= n) step(j + 1, KA1, VT0);
+  }
+  if (lead) lds_barrier();
 
   // O = O^T^T / l: lane -> query row t, register r -> d 32 dt + 8 (r/4) + 4 hl + r%4
   const float ltot = wave_swap32_sum(lsum);
@@ -206,18 +282,29 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void fwd_kernel(
   }
 }
 
-hipError_t launch_fwd(const Problem& pb, const void* q, const void* k, const void* v, void* o,
+hipError_t launch_xpose_kv(const Problem& pb, const void* src, void* dst, const KeyBlock* blocks_dev,
+                           int n_blocks, hipStream_t stream) {
+  if (n_blocks == 0) return hipSuccess;
+  dim3 grid(n_blocks, pb.Hkv), block(256);
+  if (pb.d == 128)
+    hipLaunchKernelGGL(xpose_kv_kernel<128>, grid, block, 0, stream, (const u16*)src, (u16*)dst,
+                       blocks_dev, pb.Hkv);
+  else
+    hipLaunchKernelGGL(xpose_kv_kernel<64>, grid, block, 0, stream, (const u16*)src, (u16*)dst,
+                       blocks_dev, pb.Hkv);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const Problem& pb, const void* q, const void* k, const void* vt, void* o,
                       float* lse, const FwdItem* items_dev, int n_items, hipStream_t stream) {
   if (n_items == 0) return hipSuccess;
   HeadMap hm = make_headmap(n_items, pb.Hq);
   dim3 grid(headmap_grid(hm)), block(64 * kFwdWaves);
   const float c = pb.scale * kLog2e;
-  if (pb.d == 128)
-    hipLaunchKernelGGL(fwd_kernel<128>, grid, block, 0, stream, (const u16*)q, (const u16*)k,
-                       (const u16*)v, (u16*)o, lse, items_dev, hm, pb.T, pb.Hq, pb.Hkv, c);
-  else
-    hipLaunchKernelGGL(fwd_kernel<64>, grid, block, 0, stream, (const u16*)q, (const u16*)k,
-                       (const u16*)v, (u16*)o, lse, items_dev, hm, pb.T, pb.Hq, pb.Hkv, c);
+  auto kern = pb.d == 128 ? (c == 0.f ? fwd_kernel<128, true> : fwd_kernel<128, false>)
+                          : (c == 0.f ? fwd_kernel<64, true> : fwd_kernel<64, false>);
+  hipLaunchKernelGGL(kern, grid, block, 0, stream, (const u16*)q, (const u16*)k, (const u16*)vt,
+                     (u16*)o, lse, items_dev, hm, pb.T, pb.Hq, pb.Hkv, c);
   return hipGetLastError();
 }
 
