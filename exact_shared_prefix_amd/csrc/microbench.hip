@@ -215,7 +215,44 @@ __global__ __launch_bounds__(256) void mix_kernel(float* out, int iters, float s
   out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// Dependent MFMA chains: CH independent accumulators per wave, each MFMA
+// accumulating onto the previous one of its chain (as in a k-loop).
+template <int CH>
+__global__ __launch_bounds__(256) void mfma_chain_kernel(float* out, int iters, float seed) {
+  bf16x8 a, b;
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(seed * (float)(threadIdx.x + e));
+    b[e] = (__bf16)(seed * (float)(e - (int)threadIdx.x));
+  }
+  f32x16 c[CH];
+#pragma unroll
+  for (int u = 0; u < CH; ++u) c[u] = f32x16{};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int r = 0; r < 8 / CH; ++r)
+#pragma unroll
+      for (int u = 0; u < CH; ++u) c[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[u], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int u = 0; u < CH; ++u)
+    for (int r = 0; r < 16; ++r) s += c[u][r];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 extern "C" {
+
+// blocks x 256 threads x iters x 8 MFMAs in `chains` dependent chains (1, 2, 4, 8).
+int dkv_mb_mfma_chain(int chains, int blocks, int iters, float* out, void* stream) {
+  const dim3 g(blocks), b(256);
+  hipStream_t st = (hipStream_t)stream;
+  if (chains == 1) hipLaunchKernelGGL(mfma_chain_kernel<1>, g, b, 0, st, out, iters, 1e-3f);
+  else if (chains == 2) hipLaunchKernelGGL(mfma_chain_kernel<2>, g, b, 0, st, out, iters, 1e-3f);
+  else if (chains == 4) hipLaunchKernelGGL(mfma_chain_kernel<4>, g, b, 0, st, out, iters, 1e-3f);
+  else if (chains == 8) hipLaunchKernelGGL(mfma_chain_kernel<8>, g, b, 0, st, out, iters, 1e-3f);
+  else return (int)hipErrorInvalidValue;
+  return (int)hipGetLastError();
+}
 
 // VALU rate: blocks x 256 threads x iters x 8 operations of kind op (0 exp2,
 // 1 fma, 2 cvt_pk_bf16).

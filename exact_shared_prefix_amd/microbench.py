@@ -36,6 +36,9 @@ def _load():
         _lib.dkv_mb_mix.restype = ctypes.c_int
         _lib.dkv_mb_mix.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                     ctypes.c_void_p]
+        _lib.dkv_mb_mfma_chain.restype = ctypes.c_int
+        _lib.dkv_mb_mfma_chain.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                           ctypes.c_void_p]
         _lib.dkv_mb_copy.restype = ctypes.c_int
         _lib.dkv_mb_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p]
     return _lib
@@ -142,6 +145,19 @@ def valu_cycles_per_instruction(iters: int = 8192) -> dict:
             sec = _time(lambda b, it, o, s: lib.dkv_mb_valu(op, b, it, o, s), blocks, iters)
             insts_per_simd = blocks * 4 * iters * 8 / (cu_count() * 4)
             res[f"{name}_{4 * wg}waves"] = sec * clock_hz() / insts_per_simd
+    return res
+
+
+def mfma_chain_cycles(iters: int = 2048) -> dict:
+    """SIMD cycles per 32x32x16 MFMA (reported clock) with 1, 2, 4, 8
+    dependent accumulator chains per wave, at 1 and 2 waves per SIMD."""
+    lib = _load()
+    res = {}
+    for wg in (1, 2):
+        blocks = cu_count() * wg
+        for ch in (1, 2, 4, 8):
+            sec = _time(lambda b, it, o, s: lib.dkv_mb_mfma_chain(ch, b, it, o, s), blocks, iters)
+            res[f"{ch}chains_{wg}waves"] = sec * clock_hz() / (iters * 8 * wg)
     return res
 
 
