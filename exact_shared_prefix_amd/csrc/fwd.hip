@@ -18,9 +18,9 @@
 //  * the two waves of a SIMD run one phase apart, so one issues its matrix
 //    products while the other computes its softmax;
 //  * scores are kept in the log2 domain (scale * log2 e folded in), exp2 on the
-//    transcendental unit; the running max moves only when a row's max grows
-//    by more than 2^8, so the O rescale is skipped in almost every tile; LSE
-//    is written in natural log.
+//    transcendental unit, against a reference that is only moved (with an O
+//    rescale) when the exponentials outgrow 2^20: no per-tile row max in the
+//    common case; LSE is written in natural log.
 #include "common.h"
 #include "frag.h"
 
@@ -200,33 +200,40 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void fwd_kernel(
           if (jj >= ke || jj > t) s[kb2][r] = -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    // P^T against the current reference m2 first; the reference only moves
+    // (and O, l are rescaled) when some lane's sum leaves (0, 2^20] bounds, i.e.
+    // a score exceeds m2 by about 20 (log2 units): the first tile, and rarely
+    // later. O / l and the LSE do not depend on the reference.
+    auto expo = [&]() __attribute__((always_inline)) {
+      float ps = 0.f;
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        f32x16 x;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb2][r]);
-    mx = wave_swap32_max(mx);
-    // lazy rescaling: the reference max only moves when some row's max exceeds
-    // it by more than 8 (log2 units); O / l and the LSE do not depend on it
-    if (__any(mx * c > m2 + 8.f)) {
+        for (int r = 0; r < 16; ++r) {
+          x[r] = fast_exp2(fmaf(s[kb2][r], c, -m2));
+          if (ZERO_SCALE && need_mask && s[kb2][r] == -INFINITY) x[r] = 0.f;
+          ps += x[r];
+        }
+        pack2(x, pf[kb2][0], pf[kb2][1]);
+      }
+      return ps;
+    };
+    float ps = expo();
+    if (!__all(ps <= 1048576.f)) {   // > 2^20, inf or NaN in some lane
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb2][r]);
+      mx = wave_swap32_max(mx);
       const float mnew = fmaxf(m2, mx * c);
       const float alpha = fast_exp2(m2 - mnew);
       m2 = mnew;
       lsum *= alpha;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
-    }
-    float ps = 0.f;
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = fast_exp2(fmaf(s[kb2][r], c, -m2));
-        if (ZERO_SCALE && need_mask && s[kb2][r] == -INFINITY) x = 0.f;
-        s[kb2][r] = x;
-        ps += x;
-      }
-      pack2(s[kb2], pf[kb2][0], pf[kb2][1]);
+      ps = expo();
     }
     lsum += ps;
   };
