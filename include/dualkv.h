@@ -27,7 +27,8 @@
  *    offsets non-decreasing and offsets[N] == T (R is ignored). Empty
  *    responses (R_n = 0) and P == 0 (the replicated, unshared layout) are
  *    allowed.
- *  - Supported head_dim d: 64, 128. T < 2^31 and T * max(Hq, Hkv) * d < 2^40.
+ *  - Supported head_dim d: 64, 128. T < 2^31, T * max(Hq, Hkv) * d < 2^40
+ *    and Hkv * d < 2^20.
  *  - Ownership: the caller owns every device buffer, including the
  *    workspace; the library allocates no device memory. Its only state is a
  *    small ring of pinned host staging buffers (grown on demand, kept for the
@@ -64,8 +65,10 @@ typedef enum {
   DUALKV_ERR_HIP = 4
 } dualkv_status;
 
-/* Workspace (device bytes) dualkv_fwd needs for this problem; 0 if the
- * arguments are invalid. Pure host computation. */
+/* Workspace (device bytes) dualkv_fwd needs for this problem: the work
+ * list, the 32-key block list and V^T fragments written by a transpose pass
+ * over v (about the size of v). 0 if the arguments are invalid. Pure host
+ * computation. */
 size_t dualkv_fwd_workspace_bytes(int P, int R, int N, const int32_t* offsets,
                                   int Hq, int Hkv, int d);
 
@@ -79,7 +82,8 @@ size_t dualkv_bwd_workspace_bytes(int P, int R, int N, const int32_t* offsets,
 
 /* Forward pass (DualKV pages, p1 "Approach" / p2 abstract: one launch that
  * walks the prompt KV region and then the row's own response KV region).
- * Reads q, k, v; writes o (bf16) and lse (fp32, natural log). */
+ * Reads q, k, v; writes o (bf16) and lse (fp32, natural log), and the V^T
+ * fragments into the workspace (two launches on `stream`). */
 dualkv_status dualkv_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                          int P, int R, int N, const int32_t* offsets,
                          int Hq, int Hkv, int d, float softmax_scale,
