@@ -2,8 +2,9 @@
 
 The forward and backward passes are HIP kernels in libdualkv.so behind the C
 ABI of include/dualkv.h; this package is the thin Python binding over it
-(`fwd`, `bwd`, `DualKVAttention`), plus seeded workload inputs and work/FLOP
-accounting used by the tests and the benchmark.
+(`fwd`, `bwd`, `DualKVAttention`; `fwd_groups`, `bwd_groups` for several
+prompt groups per call), plus seeded workload inputs and work/FLOP accounting
+used by the tests and the benchmark.
 """
-from .binding import (DualKVAttention, DualKVError, Packing, bwd, bwd_workspace_bytes,  # noqa: F401
-                      fwd, fwd_workspace_bytes, load)
+from .binding import (DualKVAttention, DualKVError, GroupPacking, Packing, bwd,  # noqa: F401
+                      bwd_groups, bwd_workspace_bytes, fwd, fwd_groups, fwd_workspace_bytes, load)

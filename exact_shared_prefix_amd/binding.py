@@ -18,7 +18,9 @@ LIB_PATH = os.path.join(_PKG, "libdualkv.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 EXPORTS = ("dualkv_fwd_workspace_bytes", "dualkv_bwd_workspace_bytes", "dualkv_fwd",
-           "dualkv_bwd", "dualkv_bwd_phases", "dualkv_status_string")
+           "dualkv_bwd", "dualkv_bwd_phases", "dualkv_status_string",
+           "dualkv_fwd_workspace_bytes_groups", "dualkv_bwd_workspace_bytes_groups",
+           "dualkv_fwd_groups", "dualkv_bwd_groups")
 PHASE_PRE, PHASE_MAIN, PHASE_FINISH, PHASE_DQ, PHASE_ALL = 1, 2, 4, 8, 15
 
 _lib = None
@@ -53,6 +55,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                c_int, c_int, c_int, c_float, c_int, vp, c_size, vp]
     lib.dualkv_bwd_phases.restype = c_int
     lib.dualkv_bwd_phases.argtypes = lib.dualkv_bwd.argtypes + [c_int]
+    gargs = [c_int, i32p, i32p, i32p, c_int, c_int, c_int]
+    lib.dualkv_fwd_workspace_bytes_groups.restype = c_size
+    lib.dualkv_fwd_workspace_bytes_groups.argtypes = gargs
+    lib.dualkv_bwd_workspace_bytes_groups.restype = c_size
+    lib.dualkv_bwd_workspace_bytes_groups.argtypes = gargs + [c_int]
+    lib.dualkv_fwd_groups.restype = c_int
+    lib.dualkv_fwd_groups.argtypes = [vp, vp, vp, vp, vp] + gargs + [c_float, vp, c_size, vp]
+    lib.dualkv_bwd_groups.restype = c_int
+    lib.dualkv_bwd_groups.argtypes = [vp] * 9 + gargs + [c_float, c_int, vp, c_size, vp]
     lib.dualkv_status_string.restype = ctypes.c_char_p
     lib.dualkv_status_string.argtypes = [c_int]
     _lib = lib
@@ -93,6 +104,26 @@ class Packing:
         if self.uniform:
             return None
         return ctypes.cast(self._offsets, ctypes.POINTER(ctypes.c_int32))
+
+
+class GroupPacking:
+    """Several shared-prompt groups packed back to back: groups is a sequence
+    of (P_b, response lengths of group b)."""
+
+    def __init__(self, groups: Sequence):
+        self.groups = [(int(P), [int(x) for x in L]) for P, L in groups]
+        self.B = len(self.groups)
+        self.T = sum(P + sum(L) for P, L in self.groups)
+        n_resp = sum(len(L) for _, L in self.groups)
+        self._P = (ctypes.c_int32 * max(1, self.B))(*[P for P, _ in self.groups])
+        self._N = (ctypes.c_int32 * max(1, self.B))(*[len(L) for _, L in self.groups])
+        self._R = (ctypes.c_int32 * max(1, n_resp))(*[x for _, L in self.groups for x in L])
+        self._ws = {}
+
+    def args(self):
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        return (self.B, ctypes.cast(self._P, i32p), ctypes.cast(self._N, i32p),
+                ctypes.cast(self._R, i32p))
 
 
 def _stream_ptr(stream) -> int:
@@ -196,6 +227,64 @@ def bwd(q, k, v, o, lse, do, pk: Packing, scale: Optional[float] = None,
         _check(load().dualkv_bwd(*args))
     else:
         _check(load().dualkv_bwd_phases(*args, int(phases)))
+    return dq, dk, dv
+
+
+def fwd_groups(q, k, v, gp: GroupPacking, scale: Optional[float] = None, out=None, lse=None,
+               workspace=None, stream=None):
+    """dualkv_fwd_groups -> (o, lse); layouts as fwd()."""
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    _check_tensor("q", q, (gp.T, Hq, d), torch.bfloat16, dev)
+    _check_tensor("k", k, (gp.T, Hkv, d), torch.bfloat16, dev)
+    _check_tensor("v", v, (gp.T, Hkv, d), torch.bfloat16, dev)
+    scale = d ** -0.5 if scale is None else scale
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((Hq, gp.T), dtype=torch.float32, device=dev) if lse is None else lse
+    _check_tensor("o", out, (gp.T, Hq, d), torch.bfloat16, dev)
+    _check_tensor("lse", lse, (Hq, gp.T), torch.float32, dev)
+    key = ("fwd", Hq, Hkv, d)
+    if key not in gp._ws:
+        gp._ws[key] = load().dualkv_fwd_workspace_bytes_groups(*gp.args(), Hq, Hkv, d)
+    nws = gp._ws[key]
+    if nws == 0:
+        raise DualKVError(ERR_INVALID_ARG, "invalid problem shape")
+    if workspace is None or workspace.numel() < nws:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+    _check(load().dualkv_fwd_groups(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), *gp.args(),
+                                    Hq, Hkv, d, float(scale), _ptr(workspace), workspace.numel(),
+                                    _stream_ptr(stream)))
+    return out, lse
+
+
+def bwd_groups(q, k, v, o, lse, do, gp: GroupPacking, scale: Optional[float] = None,
+               dq=None, dk=None, dv=None, workspace=None, deterministic: bool = False,
+               stream=None):
+    """dualkv_bwd_groups -> (dq, dk, dv); layouts as bwd()."""
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    for name, t, hh in (("q", q, Hq), ("o", o, Hq), ("do", do, Hq), ("k", k, Hkv), ("v", v, Hkv)):
+        _check_tensor(name, t, (gp.T, hh, d), torch.bfloat16, dev)
+    _check_tensor("lse", lse, (Hq, gp.T), torch.float32, dev)
+    scale = d ** -0.5 if scale is None else scale
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    key = ("bwd", Hq, Hkv, d, bool(deterministic))
+    if key not in gp._ws:
+        gp._ws[key] = load().dualkv_bwd_workspace_bytes_groups(*gp.args(), Hq, Hkv, d,
+                                                               int(deterministic))
+    nws = gp._ws[key]
+    if nws == 0:
+        raise DualKVError(ERR_INVALID_ARG, "invalid problem shape")
+    if workspace is None or workspace.numel() < nws:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+    _check(load().dualkv_bwd_groups(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                                    _ptr(dq), _ptr(dk), _ptr(dv), *gp.args(), Hq, Hkv, d,
+                                    float(scale), int(deterministic), _ptr(workspace),
+                                    workspace.numel(), _stream_ptr(stream)))
     return dq, dk, dv
 
 

@@ -36,37 +36,87 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Shape checks shared by every entry point. Fills pb on success.
-dualkv_status check_shape(int P, int R, int N, const int32_t* offsets, int Hq, int Hkv, int d,
-                          Problem& pb) {
-  if (P < 0 || N < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return DUALKV_ERR_INVALID_ARG;
+// Head / size checks shared by every entry point (T already known).
+dualkv_status check_heads(long long T, int Hq, int Hkv, int d, Problem& pb) {
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return DUALKV_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return DUALKV_ERR_UNSUPPORTED;
-  long long T;
-  if (offsets) {
-    if (offsets[0] != P) return DUALKV_ERR_INVALID_ARG;
-    for (int n = 0; n < N; ++n)
-      if (offsets[n + 1] < offsets[n]) return DUALKV_ERR_INVALID_ARG;
-    T = offsets[N];
-  } else {
-    if (R < 0) return DUALKV_ERR_INVALID_ARG;
-    T = (long long)P + (long long)N * R;
-  }
   if (T >= (1LL << 31)) return DUALKV_ERR_INVALID_ARG;
   // element offsets are 64-bit everywhere; this bound keeps every launch grid
   // (one lane per 8 elements in the preprocess) well inside 32 bits
   if (T * (long long)std::max(Hq, Hkv) * d >= (1LL << 40)) return DUALKV_ERR_INVALID_ARG;
   // per-lane copy offsets within a 64-key tile are 32-bit
   if ((long long)Hkv * d >= (1LL << 20)) return DUALKV_ERR_INVALID_ARG;
-  pb.P = P;
-  pb.N = N;
-  pb.R = offsets ? 0 : R;
-  pb.offsets = offsets;
   pb.T = (int)T;
   pb.Hq = Hq;
   pb.Hkv = Hkv;
   pb.G = Hq / Hkv;
   pb.d = d;
   return DUALKV_OK;
+}
+
+// One group given by P, N and uniform R or host offsets[N + 1] (offsets[0] == P,
+// non-decreasing), starting at row `start`. Appends it to pb.groups.
+dualkv_status add_group(int start, int P, int R, int N, const int32_t* offsets, Problem& pb,
+                        long long& end) {
+  if (P < 0 || N < 1) return DUALKV_ERR_INVALID_ARG;
+  Group gr;
+  gr.start = start;
+  gr.P = P;
+  gr.off.resize(N + 1);
+  long long o = (long long)start + P;
+  if (offsets) {
+    if (offsets[0] != P) return DUALKV_ERR_INVALID_ARG;
+    for (int n = 0; n < N; ++n)
+      if (offsets[n + 1] < offsets[n]) return DUALKV_ERR_INVALID_ARG;
+  } else if (R < 0) {
+    return DUALKV_ERR_INVALID_ARG;
+  }
+  for (int n = 0; n <= N; ++n) {
+    const long long on = offsets ? (long long)start + offsets[n] : o + (long long)n * R;
+    if (on >= (1LL << 31)) return DUALKV_ERR_INVALID_ARG;
+    gr.off[n] = (int)on;
+  }
+  end = gr.off[N];
+  pb.groups.push_back(std::move(gr));
+  return DUALKV_OK;
+}
+
+// Single-group problem (the dualkv_fwd / dualkv_bwd arguments).
+dualkv_status check_shape(int P, int R, int N, const int32_t* offsets, int Hq, int Hkv, int d,
+                          Problem& pb) {
+  pb.groups.clear();
+  long long T = 0;
+  const dualkv_status st = add_group(0, P, R, N, offsets, pb, T);
+  if (st != DUALKV_OK) return st;
+  return check_heads(T, Hq, Hkv, d, pb);
+}
+
+// B groups back to back (the *_groups entry points): group b has prompt length
+// group_P[b] and group_N[b] responses whose lengths are group_R[...] taken in
+// order (sum of group_N entries in all).
+dualkv_status check_groups(int B, const int32_t* group_P, const int32_t* group_N,
+                           const int32_t* resp_len, int Hq, int Hkv, int d, Problem& pb) {
+  pb.groups.clear();
+  if (B < 1 || !group_P || !group_N || !resp_len) return DUALKV_ERR_INVALID_ARG;
+  long long start = 0;
+  size_t r = 0;
+  std::vector<int32_t> offs;
+  for (int b = 0; b < B; ++b) {
+    const int N = group_N[b];
+    if (N < 1 || group_P[b] < 0 || start >= (1LL << 31)) return DUALKV_ERR_INVALID_ARG;
+    offs.assign(1, group_P[b]);
+    for (int n = 0; n < N; ++n, ++r) {
+      if (resp_len[r] < 0) return DUALKV_ERR_INVALID_ARG;
+      const long long o = (long long)offs.back() + resp_len[r];
+      if (o >= (1LL << 31)) return DUALKV_ERR_INVALID_ARG;
+      offs.push_back((int32_t)o);
+    }
+    long long end = 0;
+    const dualkv_status st = add_group((int)start, group_P[b], 0, N, offs.data(), pb, end);
+    if (st != DUALKV_OK) return st;
+    start = end;
+  }
+  return check_heads(start, Hq, Hkv, d, pb);
 }
 
 bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -124,16 +174,23 @@ hipError_t upload(void* dst, const void* src, size_t n, hipStream_t stream) {
   return staging->upload(dst, src, n, stream);
 }
 
-// 32-key blocks of the transposed K / V fragments, cut per region (the
-// prompt, then each response); base[n] = first block of response n.
-std::vector<KeyBlock> key_blocks(const Problem& pb, std::vector<int>* base = nullptr) {
+// 32-key blocks of the transposed K / V fragments, cut per region (each
+// group's prompt, then each of its responses). prompt_base[g] = first block of
+// group g's prompt, resp_base[g][n] = first block of its response n.
+std::vector<KeyBlock> key_blocks(const Problem& pb, std::vector<int>* prompt_base = nullptr,
+                                 std::vector<std::vector<int>>* resp_base = nullptr) {
   std::vector<KeyBlock> blocks;
-  for (int kb = 0; kb < pb.P; kb += 32) blocks.push_back({kb, pb.P});
-  if (base) base->clear();
-  for (int n = 0; n < pb.N; ++n) {
-    const int a = pb.seg_start(n), b = pb.seg_start(n + 1);
-    if (base) base->push_back((int)blocks.size());
-    for (int kb = a; kb < b; kb += 32) blocks.push_back({kb, b});
+  if (prompt_base) prompt_base->clear();
+  if (resp_base) resp_base->clear();
+  for (const Group& gr : pb.groups) {
+    if (prompt_base) prompt_base->push_back((int)blocks.size());
+    for (int kb = gr.start; kb < gr.start + gr.P; kb += 32) blocks.push_back({kb, gr.start + gr.P});
+    if (resp_base) resp_base->emplace_back();
+    for (int n = 0; n < gr.N(); ++n) {
+      const int a = gr.off[n], b = gr.off[n + 1];
+      if (resp_base) resp_base->back().push_back((int)blocks.size());
+      for (int kb = a; kb < b; kb += 32) blocks.push_back({kb, b});
+    }
   }
   return blocks;
 }
@@ -141,36 +198,46 @@ std::vector<KeyBlock> key_blocks(const Problem& pb, std::vector<int>* base = nul
 // Forward (and dQ) work list: query tiles of `rows` rows that never straddle
 // a segment, longest (most keys) first so the tail of the grid is short.
 std::vector<FwdItem> fwd_items(const Problem& pb, int rows = kFwdRows) {
-  std::vector<int> base;
-  key_blocks(pb, &base);
+  std::vector<int> pbase;
+  std::vector<std::vector<int>> rbase;
+  key_blocks(pb, &pbase, &rbase);
   std::vector<FwdItem> items;
-  for (int r = 0; r < pb.P; r += rows) {
-    const int r1 = std::min(pb.P, r + rows);
-    items.push_back({r, r1, r1, r1, 0});
-  }
-  for (int n = 0; n < pb.N; ++n) {
-    const int a = pb.seg_start(n), b = pb.seg_start(n + 1);
-    for (int r = a; r < b; r += rows) items.push_back({r, std::min(b, r + rows), pb.P, a, base[n]});
+  for (size_t gi = 0; gi < pb.groups.size(); ++gi) {
+    const Group& gr = pb.groups[gi];
+    const int p0 = gr.start, p1 = gr.start + gr.P;
+    for (int r = p0; r < p1; r += rows) {
+      const int r1 = std::min(p1, r + rows);
+      items.push_back({r, r1, p0, r1, r1, pbase[gi], 0});
+    }
+    for (int n = 0; n < gr.N(); ++n) {
+      const int a = gr.off[n], b = gr.off[n + 1];
+      for (int r = a; r < b; r += rows)
+        items.push_back({r, std::min(b, r + rows), p0, p1, a, pbase[gi], rbase[gi][n]});
+    }
   }
   std::stable_sort(items.begin(), items.end(), [](const FwdItem& x, const FwdItem& y) {
-    return (x.a_end + x.r1 - x.b_start) > (y.a_end + y.r1 - y.b_start);
+    return (x.a_end - x.a_start + x.r1 - x.b_start) > (y.a_end - y.a_start + y.r1 - y.b_start);
   });
   return items;
 }
 
 // dK/dV work list: kBwdKeys-key tiles, each paired with the rows that attend it
-// (all later rows for a prompt tile, the later rows of its own response for a
-// response tile), cut on a fixed grid of kBwdChunk-row chunks. Items are
-// ordered chunk-major so workgroups running together share query rows. With
-// tiles != null, also returns each tile's items (ascending) as a CSR list.
+// (all later rows of its group for a prompt tile, the later rows of its own
+// response for a response tile), cut on a fixed grid of kBwdChunk-row chunks.
+// Items are ordered chunk-major so workgroups running together share query
+// rows. With tl_out != null, also returns each tile's items (ascending) as a
+// CSR list.
 struct TileLists { std::vector<int> off, items; };
 std::vector<BwdItem> bwd_items(const Problem& pb, TileLists* tl_out = nullptr) {
   struct Tile { int kb, ke, rend; };
   std::vector<Tile> tiles;
-  for (int kb = 0; kb < pb.P; kb += kBwdKeys) tiles.push_back({kb, std::min(pb.P, kb + kBwdKeys), pb.T});
-  for (int n = 0; n < pb.N; ++n) {
-    const int a = pb.seg_start(n), b = pb.seg_start(n + 1);
-    for (int kb = a; kb < b; kb += kBwdKeys) tiles.push_back({kb, std::min(b, kb + kBwdKeys), b});
+  for (const Group& gr : pb.groups) {
+    const int p1 = gr.start + gr.P;
+    for (int kb = gr.start; kb < p1; kb += kBwdKeys) tiles.push_back({kb, std::min(p1, kb + kBwdKeys), gr.end()});
+    for (int n = 0; n < gr.N(); ++n) {
+      const int a = gr.off[n], b = gr.off[n + 1];
+      for (int kb = a; kb < b; kb += kBwdKeys) tiles.push_back({kb, std::min(b, kb + kBwdKeys), b});
+    }
   }
   std::vector<BwdItem> items;
   std::vector<std::vector<int>> per_tile(tiles.size());
@@ -237,34 +304,20 @@ BwdLayout bwd_layout(const Problem& pb, size_t n_items, size_t n_qitems, bool de
   return L;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t dualkv_fwd_workspace_bytes(int P, int R, int N, const int32_t* offsets, int Hq, int Hkv,
-                                  int d) {
-  Problem pb;
-  if (check_shape(P, R, N, offsets, Hq, Hkv, d, pb) != DUALKV_OK) return 0;
+size_t fwd_ws_bytes(const Problem& pb) {
   return fwd_layout(pb, fwd_items(pb).size(), key_blocks(pb).size()).total;
 }
 
-size_t dualkv_bwd_workspace_bytes(int P, int R, int N, const int32_t* offsets, int Hq, int Hkv,
-                                  int d, int deterministic) {
-  Problem pb;
-  if (check_shape(P, R, N, offsets, Hq, Hkv, d, pb) != DUALKV_OK) return 0;
+size_t bwd_ws_bytes(const Problem& pb, bool det) {
   TileLists tl;
   const size_t ni = bwd_items(pb, &tl).size();
   return bwd_layout(pb, std::max<size_t>(1, ni), std::max<size_t>(1, fwd_items(pb, kDqRows).size()),
-                    deterministic != 0, tl.off.size() - 1).total;
+                    det, tl.off.size() - 1).total;
 }
 
-dualkv_status dualkv_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int P,
-                         int R, int N, const int32_t* offsets, int Hq, int Hkv, int d,
-                         float softmax_scale, void* workspace, size_t workspace_bytes,
-                         void* stream) {
-  Problem pb;
-  dualkv_status st = check_shape(P, R, N, offsets, Hq, Hkv, d, pb);
-  if (st != DUALKV_OK) return st;
+dualkv_status fwd_impl(Problem& pb, const void* q, const void* k, const void* v, void* o,
+                       float* lse, float softmax_scale, void* workspace, size_t workspace_bytes,
+                       void* stream) {
   if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return DUALKV_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return DUALKV_ERR_INVALID_ARG;
@@ -278,7 +331,8 @@ dualkv_status dualkv_fwd(const void* q, const void* k, const void* v, void* o, f
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   if (upload(ws + L.items, items.data(), items.size() * sizeof(FwdItem), s) != hipSuccess ||
-      upload(ws + L.blocks, blocks.data(), blocks.size() * sizeof(KeyBlock), s) != hipSuccess)
+      (!blocks.empty() &&
+       upload(ws + L.blocks, blocks.data(), blocks.size() * sizeof(KeyBlock), s) != hipSuccess))
     return DUALKV_ERR_HIP;
   if (launch_xpose_kv(pb, v, ws + L.vt, reinterpret_cast<const KeyBlock*>(ws + L.blocks),
                       (int)blocks.size(), s) != hipSuccess ||
@@ -288,14 +342,10 @@ dualkv_status dualkv_fwd(const void* q, const void* k, const void* v, void* o, f
   return DUALKV_OK;
 }
 
-dualkv_status dualkv_bwd_phases(const void* q, const void* k, const void* v, const void* o,
-                                const float* lse, const void* dO, void* dQ, void* dK, void* dV,
-                                int P, int R, int N, const int32_t* offsets, int Hq, int Hkv,
-                                int d, float softmax_scale, int deterministic, void* workspace,
-                                size_t workspace_bytes, void* stream, int phase_mask) {
-  Problem pb;
-  dualkv_status st = check_shape(P, R, N, offsets, Hq, Hkv, d, pb);
-  if (st != DUALKV_OK) return st;
+dualkv_status bwd_impl(Problem& pb, const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dO, void* dQ, void* dK, void* dV,
+                       float softmax_scale, int deterministic, void* workspace,
+                       size_t workspace_bytes, void* stream, int phase_mask) {
   if (phase_mask < 1 || phase_mask > 15) return DUALKV_ERR_INVALID_ARG;
   if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return DUALKV_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
@@ -339,6 +389,46 @@ dualkv_status dualkv_bwd_phases(const void* q, const void* k, const void* v, con
   return DUALKV_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+size_t dualkv_fwd_workspace_bytes(int P, int R, int N, const int32_t* offsets, int Hq, int Hkv,
+                                  int d) {
+  Problem pb;
+  if (check_shape(P, R, N, offsets, Hq, Hkv, d, pb) != DUALKV_OK) return 0;
+  return fwd_ws_bytes(pb);
+}
+
+size_t dualkv_bwd_workspace_bytes(int P, int R, int N, const int32_t* offsets, int Hq, int Hkv,
+                                  int d, int deterministic) {
+  Problem pb;
+  if (check_shape(P, R, N, offsets, Hq, Hkv, d, pb) != DUALKV_OK) return 0;
+  return bwd_ws_bytes(pb, deterministic != 0);
+}
+
+dualkv_status dualkv_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int P,
+                         int R, int N, const int32_t* offsets, int Hq, int Hkv, int d,
+                         float softmax_scale, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  Problem pb;
+  const dualkv_status st = check_shape(P, R, N, offsets, Hq, Hkv, d, pb);
+  if (st != DUALKV_OK) return st;
+  return fwd_impl(pb, q, k, v, o, lse, softmax_scale, workspace, workspace_bytes, stream);
+}
+
+dualkv_status dualkv_bwd_phases(const void* q, const void* k, const void* v, const void* o,
+                                const float* lse, const void* dO, void* dQ, void* dK, void* dV,
+                                int P, int R, int N, const int32_t* offsets, int Hq, int Hkv,
+                                int d, float softmax_scale, int deterministic, void* workspace,
+                                size_t workspace_bytes, void* stream, int phase_mask) {
+  Problem pb;
+  const dualkv_status st = check_shape(P, R, N, offsets, Hq, Hkv, d, pb);
+  if (st != DUALKV_OK) return st;
+  return bwd_impl(pb, q, k, v, o, lse, dO, dQ, dK, dV, softmax_scale, deterministic, workspace,
+                  workspace_bytes, stream, phase_mask);
+}
+
 dualkv_status dualkv_bwd(const void* q, const void* k, const void* v, const void* o,
                          const float* lse, const void* dO, void* dQ, void* dK, void* dV, int P,
                          int R, int N, const int32_t* offsets, int Hq, int Hkv, int d,
@@ -346,6 +436,45 @@ dualkv_status dualkv_bwd(const void* q, const void* k, const void* v, const void
                          size_t workspace_bytes, void* stream) {
   return dualkv_bwd_phases(q, k, v, o, lse, dO, dQ, dK, dV, P, R, N, offsets, Hq, Hkv, d,
                            softmax_scale, deterministic, workspace, workspace_bytes, stream, 15);
+}
+
+size_t dualkv_fwd_workspace_bytes_groups(int B, const int32_t* group_P, const int32_t* group_N,
+                                         const int32_t* resp_len, int Hq, int Hkv, int d) {
+  Problem pb;
+  if (check_groups(B, group_P, group_N, resp_len, Hq, Hkv, d, pb) != DUALKV_OK) return 0;
+  return fwd_ws_bytes(pb);
+}
+
+size_t dualkv_bwd_workspace_bytes_groups(int B, const int32_t* group_P, const int32_t* group_N,
+                                         const int32_t* resp_len, int Hq, int Hkv, int d,
+                                         int deterministic) {
+  Problem pb;
+  if (check_groups(B, group_P, group_N, resp_len, Hq, Hkv, d, pb) != DUALKV_OK) return 0;
+  return bwd_ws_bytes(pb, deterministic != 0);
+}
+
+dualkv_status dualkv_fwd_groups(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, const int32_t* group_P, const int32_t* group_N,
+                                const int32_t* resp_len, int Hq, int Hkv, int d,
+                                float softmax_scale, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  Problem pb;
+  const dualkv_status st = check_groups(B, group_P, group_N, resp_len, Hq, Hkv, d, pb);
+  if (st != DUALKV_OK) return st;
+  return fwd_impl(pb, q, k, v, o, lse, softmax_scale, workspace, workspace_bytes, stream);
+}
+
+dualkv_status dualkv_bwd_groups(const void* q, const void* k, const void* v, const void* o,
+                                const float* lse, const void* dO, void* dQ, void* dK, void* dV,
+                                int B, const int32_t* group_P, const int32_t* group_N,
+                                const int32_t* resp_len, int Hq, int Hkv, int d,
+                                float softmax_scale, int deterministic, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  Problem pb;
+  const dualkv_status st = check_groups(B, group_P, group_N, resp_len, Hq, Hkv, d, pb);
+  if (st != DUALKV_OK) return st;
+  return bwd_impl(pb, q, k, v, o, lse, dO, dQ, dK, dV, softmax_scale, deterministic, workspace,
+                  workspace_bytes, stream, 15);
 }
 
 const char* dualkv_status_string(dualkv_status s) {

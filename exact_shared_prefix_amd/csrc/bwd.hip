@@ -376,11 +376,11 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) dqacc[dt] = f32x16{};
 
-  const int nA = (it.a_end + BK - 1) / BK;
+  const int nA = (it.a_end - it.a_start + BK - 1) / BK;
   const int nB = it.r1 > it.b_start ? (it.r1 - it.b_start + BK - 1) / BK : 0;
   const int ntiles = nA + nB;
   auto tile_bounds = [&](int i, int& kb, int& ke) {
-    if (i < nA) { kb = i * BK; ke = it.a_end; }
+    if (i < nA) { kb = it.a_start + i * BK; ke = it.a_end; }
     else { kb = it.b_start + (i - nA) * BK; ke = it.r1; }
   };
   // copies of tile i: job f = w, w + NW, ...: tensor f / NTF, key block

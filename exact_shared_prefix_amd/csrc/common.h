@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#include <vector>
+
 namespace dkv {
 
 typedef unsigned short u16;
@@ -19,25 +21,29 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // ---------------------------------------------------------------- problem --
-// Host-side description of one packed micro-batch.
+// Host-side description of one packed micro-batch: one or more shared-prompt
+// groups stored back to back. Group g's prompt is rows [start, start + P) and
+// its response n is rows [off[n], off[n + 1]) (off[0] = start + P).
+struct Group {
+  int start = 0, P = 0;
+  std::vector<int> off;
+  int N() const { return (int)off.size() - 1; }
+  int end() const { return off.back(); }
+};
 struct Problem {
-  int P = 0;          // prompt tokens
-  int N = 0;          // responses
   int T = 0;          // packed tokens
   int Hq = 0, Hkv = 0, G = 0, d = 0;
   float scale = 0.f;  // softmax scale
-  const int32_t* offsets = nullptr;  // host, N+1 entries (o_0 = P ... o_N = T)
-  int R = 0;          // uniform response length when offsets == nullptr
-  int seg_start(int n) const { return offsets ? offsets[n] : P + n * R; }
+  std::vector<Group> groups;
 };
 
 // Forward work item: query rows [r0, r1) of one segment; KV region A is
-// [0, a_end) (the prompt, or the prompt rows up to r1 for a prompt tile) and
-// region B is [b_start, r1) (the own response; empty for a prompt tile).
-// b_blk is the index of region B's first 32-key block in the transposed
-// fragment layout (blocks are cut per region: the prompt's, then each
-// response's, so a region's tiles start on a block).
-struct FwdItem { int r0, r1, a_end, b_start, b_blk; };
+// [a_start, a_end) (the group's prompt, or its prompt rows up to r1 for a
+// prompt tile) and region B is [b_start, r1) (the own response; empty for a
+// prompt tile). a_blk, b_blk are the indices of the regions' first 32-key
+// blocks in the transposed fragment layout (blocks are cut per region: each
+// prompt's, each response's, so a region's tiles start on a block).
+struct FwdItem { int r0, r1, a_start, a_end, b_start, a_blk, b_blk; };
 
 // 32-key block of the transposed fragment layout: keys [key0, key0 + 32)
 // clamped to [key0, kend) (kend = end of the block's region).

@@ -124,11 +124,11 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void fwd_kernel(
   f32x16 s[2];        // S^T of the current tile: block kb2, register r <-> key kb + 32 kb2 + 8 (r/4) + 4 hl + r%4
   bf16x8 pf[2][2];    // P^T of the previous tile, B operands of O^T += V^T P^T
 
-  const int nA = (it.a_end + BK - 1) / BK;
+  const int nA = (it.a_end - it.a_start + BK - 1) / BK;
   const int nB = it.r1 > it.b_start ? (it.r1 - it.b_start + BK - 1) / BK : 0;
   const int n = nA + nB;
   auto tile_bounds = [&](int i, int& kb, int& ke) __attribute__((always_inline)) {
-    if (i < nA) { kb = i * BK; ke = it.a_end; }
+    if (i < nA) { kb = it.a_start + i * BK; ke = it.a_end; }
     else { kb = it.b_start + (i - nA) * BK; ke = it.r1; }
   };
   // copies of tile i by the trailing waves (copy f = (w - NL) + NL j):
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void fwd_kernel(
   auto copy_vt = [&](int i, u16* dst) __attribute__((always_inline)) {
     int kb, ke;
     tile_bounds(i, kb, ke);
-    const int b0 = i < nA ? kb / 32 : it.b_blk + (kb - it.b_start) / 32;
+    const int b0 = i < nA ? it.a_blk + (kb - it.a_start) / 32 : it.b_blk + (kb - it.b_start) / 32;
     const int blast = b0 + (ke - 1 - kb) / 32;
 #pragma unroll
     for (int j = 0; j < NC; ++j) {

@@ -119,6 +119,38 @@ dualkv_status dualkv_bwd_phases(const void* q, const void* k, const void* v, con
                                 void* workspace, size_t workspace_bytes, void* stream,
                                 int phase_mask);
 
+/* Several shared-prompt groups in one call. The DualKV summary page quotes its
+ * GRPO speed-ups at a micro-batch size of 8 ("Key results") and states that
+ * one shared prefix is assumed per micro-batch group ("Limitations"); the
+ * reading taken here is that a micro-batch holds several such groups. The B groups are packed back to back in the same
+ * [T][H][d] tensors: group b occupies rows [s_b, s_{b+1}) with s_0 = 0; its
+ * first group_P[b] rows are its prompt, followed by its group_N[b] responses,
+ * whose lengths are the next group_N[b] entries of resp_len (HOST int32 arrays:
+ * group_P and group_N of B entries, resp_len of sum(group_N) entries). A row
+ * attends only keys of its own group, by the single-group rule (prompt rows:
+ * causal within the group's prompt; response rows: the group's whole prompt and
+ * their own response causally). Groups are independent: the result equals one
+ * single-group call per group on its rows. Every other convention (layouts,
+ * LSE, scale, workspace, asynchrony, errors; group_N[b] >= 1, group_P[b] >= 0,
+ * resp_len >= 0, B >= 1, NULL arrays are DUALKV_ERR_INVALID_ARG) is that of
+ * the single-group entry points, which are the B = 1 case. */
+size_t dualkv_fwd_workspace_bytes_groups(int B, const int32_t* group_P, const int32_t* group_N,
+                                         const int32_t* resp_len, int Hq, int Hkv, int d);
+size_t dualkv_bwd_workspace_bytes_groups(int B, const int32_t* group_P, const int32_t* group_N,
+                                         const int32_t* resp_len, int Hq, int Hkv, int d,
+                                         int deterministic);
+dualkv_status dualkv_fwd_groups(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, const int32_t* group_P, const int32_t* group_N,
+                                const int32_t* resp_len, int Hq, int Hkv, int d,
+                                float softmax_scale, void* workspace, size_t workspace_bytes,
+                                void* stream);
+dualkv_status dualkv_bwd_groups(const void* q, const void* k, const void* v, const void* o,
+                                const float* lse, const void* dO, void* dQ, void* dK, void* dV,
+                                int B, const int32_t* group_P, const int32_t* group_N,
+                                const int32_t* resp_len, int Hq, int Hkv, int d,
+                                float softmax_scale, int deterministic, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Static English description of a status code (never NULL). */
 const char* dualkv_status_string(dualkv_status s);
 

@@ -18,9 +18,13 @@ Two independent formulations of the same definition live here:
   of response n. It evaluates selected rows/keys at full workload sizes, where
   the literal replication is too slow to run whole.
 
-Every function in both modules has a pin in tests/test_oracle.py against
+``groups`` extends both to several shared-prompt groups packed back to back
+(independent groups; each row attends only its own group).
+
+Every function in these modules has a pin in tests/test_oracle.py against
 something other than itself (library attention + autograd, closed forms,
 finite differences, invariants).
 """
 from .replicated import oracle_fwd_bwd, causal_attention_fwd, causal_attention_bwd  # noqa: F401
 from .sampled import attended_keys, rows_fwd_bwd, keys_dkdv  # noqa: F401
+from .groups import attended_keys_groups, group_starts, oracle_groups_fwd_bwd  # noqa: F401

@@ -134,6 +134,62 @@ def test_workspace_sizes(lib):
     assert not rag.uniform and pk.uniform
 
 
+def _arr(xs):
+    if xs is None:
+        return None
+    a = (ctypes.c_int32 * max(1, len(xs)))(*xs)
+    return ctypes.cast(a, ctypes.POINTER(ctypes.c_int32))
+
+
+def _fwd_groups(lib, B=2, gP=(16, 8), gN=(2, 1), R=(8, 4, 5), Hq=4, Hkv=2, d=128, scale=0.1,
+                ws=FAKE, ws_bytes=1 << 20):
+    return lib.dualkv_fwd_groups(FAKE, FAKE, FAKE, FAKE, FAKE, B, _arr(gP), _arr(gN), _arr(R), Hq,
+                                 Hkv, d, scale, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), ERR_INVALID_ARG),
+    (dict(gP=None), ERR_INVALID_ARG),
+    (dict(gN=None), ERR_INVALID_ARG),
+    (dict(R=None), ERR_INVALID_ARG),
+    (dict(gN=(2, 0)), ERR_INVALID_ARG),        # a group without responses
+    (dict(gP=(16, -1)), ERR_INVALID_ARG),
+    (dict(R=(8, -4, 5)), ERR_INVALID_ARG),
+    (dict(R=(8, 1 << 30, 1 << 30)), ERR_INVALID_ARG),   # T >= 2^31
+    (dict(Hq=3), ERR_INVALID_ARG),
+    (dict(d=96), ERR_UNSUPPORTED),
+    (dict(scale=-1.0), ERR_INVALID_ARG),
+    (dict(ws_bytes=16), ERR_WORKSPACE),
+])
+def test_fwd_groups_rejects_bad_arguments(lib, kw, status):
+    assert _fwd_groups(lib, **kw) == status
+
+
+def test_bwd_groups_rejects_bad_arguments(lib):
+    gP, gN, R = _arr((16, 8)), _arr((2, 1)), _arr((8, 4, 5))
+    call = lambda B, ws_bytes, det=0: lib.dualkv_bwd_groups(  # noqa: E731
+        FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B, gP, gN, R, 4, 2, 128, 0.1, det,
+        FAKE, ws_bytes, None)
+    assert call(0, 1 << 20) == ERR_INVALID_ARG
+    assert call(2, 16) == ERR_WORKSPACE
+    assert call(2, 16, det=1) == ERR_WORKSPACE
+
+
+def test_group_workspace_sizes(lib):
+    # one group is the single-group problem
+    for det in (0, 1):
+        one = lib.dualkv_bwd_workspace_bytes_groups(1, _arr((16,)), _arr((3,)), _arr((8, 0, 5)),
+                                                    4, 2, 128, det)
+        ref = lib.dualkv_bwd_workspace_bytes(16, 0, 3, _arr((16, 24, 24, 29)), 4, 2, 128, det)
+        assert one == ref > 0
+    one = lib.dualkv_fwd_workspace_bytes_groups(1, _arr((16,)), _arr((3,)), _arr((8, 0, 5)), 4, 2, 128)
+    assert one == lib.dualkv_fwd_workspace_bytes(16, 0, 3, _arr((16, 24, 24, 29)), 4, 2, 128) > 0
+    two = lib.dualkv_fwd_workspace_bytes_groups(2, _arr((16, 8)), _arr((3, 1)), _arr((8, 0, 5, 4)),
+                                                4, 2, 128)
+    assert two > one and two % 256 == 0
+    assert lib.dualkv_fwd_workspace_bytes_groups(0, _arr((16,)), _arr((3,)), _arr((8,)), 4, 2, 128) == 0
+
+
 def test_pair_accounting_matches_brute_force():
     from oracle import attended_keys
     for P, lengths in ((5, [3, 0, 4]), (0, [6, 2]), (9, [1])):

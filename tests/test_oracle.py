@@ -328,3 +328,101 @@ def test_ragged_lengths_draw():
     lens = response_lengths(w)
     assert len(lens) == 16 and all(256 <= x <= 2048 for x in lens)
     assert lens == response_lengths(w)  # deterministic
+
+
+# --------------------------------------------------- several prompt groups --
+from oracle import attended_keys_groups, group_starts, oracle_groups_fwd_bwd  # noqa: E402
+
+
+def _groups_attended(t, groups):
+    """A(t) of a multi-group batch written out independently: find the group
+    holding row t, then the single-group rule inside it, in absolute indices."""
+    start = 0
+    for P, L in groups:
+        size = P + sum(L)
+        if t < start + size:
+            return [start + j for j in _attended(t - start, P, L)]
+        start += size
+    raise IndexError(t)
+
+
+def _dense_masked_reference(q, k, v, do, groups, scale):
+    """Dense attention over the whole packed tensor with an explicit boolean
+    mask M[t, j] = (j in A(t)), float64, gradients of L = sum <dO, O> by
+    autograd: a formulation with no replication and no per-group slicing."""
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    M = torch.zeros(T, T, dtype=torch.bool)
+    for t in range(T):
+        M[t, _groups_attended(t, groups)] = True
+    qt = torch.tensor(q, dtype=torch.float64, requires_grad=True)
+    kt = torch.tensor(k, dtype=torch.float64, requires_grad=True)
+    vt = torch.tensor(v, dtype=torch.float64, requires_grad=True)
+    O = torch.zeros(T, Hq, d, dtype=torch.float64)
+    LSE = torch.zeros(Hq, T, dtype=torch.float64)
+    for h in range(Hq):
+        S = scale * (qt[:, h] @ kt[:, h // G].T)
+        S = S.masked_fill(~M, float("-inf"))
+        LSE[h] = torch.logsumexp(S, dim=1)
+        O[:, h] = torch.softmax(S, dim=1) @ vt[:, h // G]
+    (O * torch.tensor(do, dtype=torch.float64)).sum().backward()
+    return {"O": O.detach().numpy(), "LSE": LSE.detach().numpy(), "dQ": qt.grad.numpy(),
+            "dK": kt.grad.numpy(), "dV": vt.grad.numpy()}
+
+
+GROUP_CASES = [
+    # (groups, Hq, Hkv, d)
+    ([(5, [3, 0, 4]), (0, [6]), (4, [2, 5])], 4, 2, 8),
+    ([(7, [1, 2]), (3, [4]), (6, [0, 3, 2])], 2, 1, 4),
+]
+
+
+@pytest.mark.parametrize("case", range(len(GROUP_CASES)))
+def test_group_oracle_matches_dense_masked_attention(case):
+    groups, Hq, Hkv, d = GROUP_CASES[case]
+    T = group_starts(groups)[-1]
+    rng = np.random.default_rng(60 + case)
+    q, do = rng.standard_normal((T, Hq, d)), rng.standard_normal((T, Hq, d))
+    k, v = rng.standard_normal((T, Hkv, d)), rng.standard_normal((T, Hkv, d))
+    scale = 0.7
+    got = oracle_groups_fwd_bwd(q, k, v, do, groups, scale)
+    ref = _dense_masked_reference(q, k, v, do, groups, scale)
+    for key in ("O", "LSE", "dQ", "dK", "dV"):
+        assert np.max(np.abs(got[key] - ref[key])) <= 1e-10, key
+
+
+def test_group_oracle_one_group_is_the_single_group_oracle():
+    inp = make_inputs(6, [3, 0, 5], 4, 2, 8, seed=61)
+    q, k, v, do = _inputs_np(inp)
+    a = oracle_groups_fwd_bwd(q, k, v, do, [(6, [3, 0, 5])], inp.scale)
+    b = oracle_fwd_bwd(q, k, v, do, 6, [3, 0, 5], inp.scale)
+    for key in ("O", "LSE", "dQ", "dK", "dV"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_groups_are_isolated():
+    """Changing every input of the middle group leaves the other groups'
+    outputs and gradients bitwise unchanged."""
+    groups = [(4, [2, 3]), (3, [5]), (2, [1, 4])]
+    s = group_starts(groups)
+    T = s[-1]
+    rng = np.random.default_rng(62)
+    x = [rng.standard_normal((T, 2, 4)) for _ in range(2)] + [rng.standard_normal((T, 1, 4)) for _ in range(2)]
+    q, do, k, v = x
+    a = oracle_groups_fwd_bwd(q, k, v, do, groups, 0.5)
+    q2, k2, v2, do2 = (t.copy() for t in (q, k, v, do))
+    for t in (q2, k2, v2, do2):
+        t[s[1]:s[2]] += rng.standard_normal(t[s[1]:s[2]].shape)
+    b = oracle_groups_fwd_bwd(q2, k2, v2, do2, groups, 0.5)
+    keep = np.r_[0:s[1], s[2]:T]
+    for key in ("O", "dQ", "dK", "dV"):
+        assert np.array_equal(a[key][keep], b[key][keep]), key
+        assert not np.allclose(a[key][s[1]:s[2]], b[key][s[1]:s[2]]), key
+    assert np.array_equal(a["LSE"][:, keep], b["LSE"][:, keep])
+
+
+def test_group_attended_keys_against_independent_definition():
+    groups = [(3, [2, 0, 1]), (0, [4]), (5, [2])]
+    for t in range(group_starts(groups)[-1]):
+        assert list(attended_keys_groups(t, groups)) == _groups_attended(t, groups)

@@ -20,11 +20,16 @@ pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 REPLICATED = os.path.join(ROOT, "oracle", "replicated.py")
 SAMPLED = os.path.join(ROOT, "oracle", "sampled.py")
+GROUPS = os.path.join(ROOT, "oracle", "groups.py")
 
 
-def _load(path, old=None, new=None, nth=1):
-    """Module from `path` with the nth occurrence of `old` replaced by `new`."""
+def _load(path, old=None, new=None, nth=1, inject=None):
+    """Module from `path` with the nth occurrence of `old` replaced by `new`.
+    inject: names to place in the module instead of its package-relative
+    imports (which a stand-alone copy cannot resolve)."""
     src = open(path).read()
+    if inject:
+        src = "\n".join(l for l in src.split("\n") if not l.startswith("from ."))
     if old is not None:
         pos = -1
         for _ in range(nth):
@@ -32,6 +37,7 @@ def _load(path, old=None, new=None, nth=1):
             assert pos >= 0, f"mutation site not found: {old!r} (occurrence {nth})"
         src = src[:pos] + new + src[pos + len(old):]
     mod = types.ModuleType("oracle_copy_" + os.path.basename(path)[:-3])
+    mod.__dict__.update(inject or {})
     exec(compile(src, path, "exec"), mod.__dict__)
     return mod
 
@@ -52,15 +58,23 @@ def _pin_calls():
         (pins.test_sampled_oracle_matches_replicated, ((0, [7, 11], 2, 1, 8),)),
         (pins.test_attended_keys_definition, ()),
         (pins.test_attended_keys_against_independent_definition, ()),
+        (pins.test_group_oracle_matches_dense_masked_attention, (0,)),
+        (pins.test_group_oracle_matches_dense_masked_attention, (1,)),
+        (pins.test_group_oracle_one_group_is_the_single_group_oracle, ()),
+        (pins.test_groups_are_isolated, ()),
+        (pins.test_group_attended_keys_against_independent_definition, ()),
     ]
     return calls
 
 
-def _failing_pins(monkeypatch, rep, smp):
+def _failing_pins(monkeypatch, rep, smp, grp):
     monkeypatch.setattr(pins, "oracle_fwd_bwd", rep.oracle_fwd_bwd)
     monkeypatch.setattr(pins, "rows_fwd_bwd", smp.rows_fwd_bwd)
     monkeypatch.setattr(pins, "keys_dkdv", smp.keys_dkdv)
     monkeypatch.setattr(pins, "attended_keys", smp.attended_keys)
+    monkeypatch.setattr(pins, "oracle_groups_fwd_bwd", grp.oracle_groups_fwd_bwd)
+    monkeypatch.setattr(pins, "attended_keys_groups", grp.attended_keys_groups)
+    monkeypatch.setattr(pins, "group_starts", grp.group_starts)
     failed = []
     with np.errstate(all="ignore"):
         for fn, args in _pin_calls():
@@ -102,17 +116,29 @@ MUTANTS = {
     "keys_dk_no_scale": (SAMPLED, "dk[hit] = scale * (dS[:, cols].T @ Qb)", "dk[hit] = dS[:, cols].T @ Qb", 1),
     "keys_skip_first_prompt_rows": (SAMPLED, "for r in range(lo, P, row_block)", "for r in range(lo + 1, P, row_block)", 1),
     "keys_gqa_one_head": (SAMPLED, "for h in range(kv_head * G, (kv_head + 1) * G)", "for h in range(kv_head * G, kv_head * G + 1)", 1),
+    # several prompt groups
+    "groups_start_not_advanced": (GROUPS, "s.append(s[-1] + int(P) + sum(int(x) for x in L))", "s.append(int(P) + sum(int(x) for x in L))", 1),
+    "groups_keys_not_shifted": (GROUPS, "return s[b] + attended_keys(t - s[b]", "return attended_keys(t - s[b]", 1),
+    "groups_dK_from_dV": (GROUPS, 'out["dK"][a:e] = r["dK"]', 'out["dK"][a:e] = r["dV"]', 1),
+    "groups_lse_shifted": (GROUPS, 'out["LSE"][:, a:e] = r["LSE"]', 'out["LSE"][:, a:e] = np.roll(r["LSE"], 1, axis=1)', 1),
 }
 
 
+def _load_all(path=None, old=None, new=None, nth=1):
+    rep = _load(REPLICATED, old, new, nth) if path == REPLICATED else _load(REPLICATED)
+    smp = _load(SAMPLED, old, new, nth) if path == SAMPLED else _load(SAMPLED)
+    inj = {"oracle_fwd_bwd": rep.oracle_fwd_bwd, "attended_keys": smp.attended_keys}
+    grp = (_load(GROUPS, old, new, nth, inject=inj) if path == GROUPS
+           else _load(GROUPS, inject=inj))
+    return rep, smp, grp
+
+
 def test_unedited_copy_passes_every_pin(monkeypatch):
-    assert _failing_pins(monkeypatch, _load(REPLICATED), _load(SAMPLED)) == []
+    assert _failing_pins(monkeypatch, *_load_all()) == []
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistake_is_caught(monkeypatch, name):
     path, old, new, nth = MUTANTS[name]
-    rep = _load(REPLICATED, old, new, nth) if path == REPLICATED else _load(REPLICATED)
-    smp = _load(SAMPLED, old, new, nth) if path == SAMPLED else _load(SAMPLED)
-    failed = _failing_pins(monkeypatch, rep, smp)
+    failed = _failing_pins(monkeypatch, *_load_all(path, old, new, nth))
     assert failed, f"no pin catches the planted mistake {name}"

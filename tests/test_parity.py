@@ -23,7 +23,7 @@ import torch
 
 from exact_shared_prefix_amd import binding
 from exact_shared_prefix_amd.inputs import WORKLOADS, make_inputs, workload_inputs
-from oracle import keys_dkdv, oracle_fwd_bwd, rows_fwd_bwd
+from oracle import group_starts, keys_dkdv, oracle_fwd_bwd, oracle_groups_fwd_bwd, rows_fwd_bwd
 
 pytestmark = pytest.mark.gpu
 
@@ -173,6 +173,60 @@ def test_deterministic_mode_bitwise_repeat_multi_chunk():
     for key in ("dQ", "dK", "dV"):
         assert np.array_equal(a[key], b[key]), key
         assert rel(a[key], c[key]) <= 1e-3, key
+
+
+# ------------------------------------------------- several prompt groups --
+GROUPS = {
+    # groups: [(P_b, [R_b0, ...]), ...]
+    "three_groups_ragged_d128": dict(groups=[(300, [129, 1, 0, 64]), (0, [200]), (129, [31, 0, 250])],
+                                     Hq=4, Hkv=2, d=128, seed=41),
+    "four_groups_d64_gqa4": dict(groups=[(64, [64, 64]), (70, [1, 2, 3]), (256, [100]), (5, [300])],
+                                 Hq=8, Hkv=2, d=64, seed=42),
+}
+
+
+def run_gpu_groups(inp, groups, deterministic=False):
+    dev = torch.device("cuda:0")
+    q, k, v, do = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.do))
+    gp = binding.GroupPacking(groups)
+    o, lse = binding.fwd_groups(q, k, v, gp, inp.scale)
+    dq, dk, dv = binding.bwd_groups(q, k, v, o, lse, do, gp, inp.scale, deterministic=deterministic)
+    torch.cuda.synchronize()
+    return {kk: t.float().cpu().numpy() for kk, t in
+            {"O": o, "LSE": lse, "dQ": dq, "dK": dk, "dV": dv}.items()}
+
+
+@pytest.mark.parametrize("name", sorted(GROUPS))
+@pytest.mark.parametrize("det", [False, True])
+def test_groups_elementwise(name, det):
+    c = GROUPS[name]
+    groups = c["groups"]
+    T = group_starts(groups)[-1]
+    inp = make_inputs(0, [T], c["Hq"], c["Hkv"], c["d"], seed=c["seed"])
+    say(f"case groups {name} det={det}: {groups}")
+    got = run_gpu_groups(inp, groups, det)
+    ref = oracle_groups_fwd_bwd(np64(inp.q), np64(inp.k), np64(inp.v), np64(inp.do), groups, inp.scale)
+    s = group_starts(groups)
+    for b in range(len(groups)):
+        a, e = s[b], s[b + 1]
+        for key in ("O", "dQ", "dK", "dV"):
+            err = rel(got[key][a:e], ref[key][a:e])
+            say(f"  group {b} {key}: rel {err:.2e}")
+            assert err <= REL, (b, key)
+        assert float(np.max(np.abs(got["LSE"][:, a:e] - ref["LSE"][:, a:e]))) <= LSE_ABS, b
+    for key, x in got.items():
+        assert np.all(np.isfinite(x)), key
+
+
+def test_one_group_call_is_the_single_group_call():
+    """B = 1 through the group entry points gives the single-group entry
+    points' bits (deterministic backward, so dK, dV are ordered too)."""
+    P, L = 300, [129, 1, 0, 64, 250]
+    inp = make_inputs(P, L, 4, 2, 128, seed=43)
+    a = run_gpu(inp, deterministic=True)
+    b = run_gpu_groups(inp, [(P, L)], deterministic=True)
+    for key in ("O", "LSE", "dQ", "dK", "dV"):
+        assert np.array_equal(a[key], b[key]), key
 
 
 # ----------------------------------------------------------- full sizes --
