@@ -202,6 +202,125 @@ def calibrate_copy(nbytes: int) -> None:
     print(json.dumps(microbench.copy(nbytes)))
 
 
+def group_main(args, name: str) -> int:
+    """Several prompt groups per call (dualkv_fwd_groups / dualkv_bwd_groups):
+    the same JSON line for a multi-group workload. The group entry points have
+    no per-phase split, so the roofline is taken over the whole fwd+bwd step
+    with the algorithmic FLOPs of all three kernels (4 d + 8 d + 6 d per pair
+    and query head)."""
+    import torch
+
+    from exact_shared_prefix_amd import binding, metrics
+    from exact_shared_prefix_amd.inputs import GROUP_WORKLOADS, group_workload_inputs
+
+    w = GROUP_WORKLOADS[name]
+    log(f"[bench] workload {name}: generating seeded inputs")
+    inp = group_workload_inputs(w)
+    groups = w.groups
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    torch.empty(1, device=dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    q, k, v, do = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.do))
+
+    def run(gp, qq, kk, vv, dd, steps, warmup):
+        o = torch.empty_like(qq)
+        lse = torch.empty((qq.shape[1], gp.T), dtype=torch.float32, device=dev)
+        dq, dk, dv = torch.empty_like(qq), torch.empty_like(kk), torch.empty_like(vv)
+        wsf = torch.empty(load_ws(gp, qq, kk, False), dtype=torch.uint8, device=dev)
+        wsb = torch.empty(load_ws(gp, qq, kk, True), dtype=torch.uint8, device=dev)
+        s = torch.cuda.current_stream()
+        for _ in range(warmup):
+            binding.fwd_groups(qq, kk, vv, gp, inp.scale, o, lse, wsf)
+            binding.bwd_groups(qq, kk, vv, o, lse, dd, gp, inp.scale, dq, dk, dv, wsb)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for e0, e1, e2 in ev:
+            e0.record(s)
+            binding.fwd_groups(qq, kk, vv, gp, inp.scale, o, lse, wsf)
+            e1.record(s)
+            binding.bwd_groups(qq, kk, vv, o, lse, dd, gp, inp.scale, dq, dk, dv, wsb)
+            e2.record(s)
+        torch.cuda.synchronize()
+        f = [a.elapsed_time(b) for a, b, _ in ev]
+        t = [a.elapsed_time(c) for a, _, c in ev]
+        return {"ms_per_step": sum(t) / steps, "min_ms_per_step": min(t),
+                "median_ms_per_step": sorted(t)[steps // 2], "fwd_ms": sum(f) / steps,
+                "bwd_ms": (sum(t) - sum(f)) / steps}
+
+    def load_ws(gp, qq, kk, bwd):
+        Hq, d, Hkv = qq.shape[1], qq.shape[2], kk.shape[1]
+        lib = binding.load()
+        if bwd:
+            return lib.dualkv_bwd_workspace_bytes_groups(*gp.args(), Hq, Hkv, d, 0)
+        return lib.dualkv_fwd_workspace_bytes_groups(*gp.args(), Hq, Hkv, d)
+
+    gp = binding.GroupPacking(groups)
+    log(f"[bench] {w.B} groups, T={gp.T}: {args.warmup} warmup + {args.steps} timed steps")
+    t = run(gp, q, k, v, do, args.steps, args.warmup)
+    peak = torch.cuda.max_memory_allocated(dev)
+    pairs = sum(metrics.pairs(P, L) for P, L in groups)
+    useful = 14 * inp.d * inp.Hq * pairs
+    executed = 18 * inp.d * inp.Hq * pairs
+    ms = t["ms_per_step"]
+    value = useful / (ms * 1e-3) / 1e12
+    log(f"[bench] {ms:.2f} ms/step, {value:.1f} useful TFLOP/s (fwd {t['fwd_ms']:.2f} ms, bwd {t['bwd_ms']:.2f} ms)")
+    rep = None
+    if not args.no_replicated:
+        # the same kernels on the unshared layout: every sequence carries its own prompt copy
+        rlen = [P + r for P, L in groups for r in L]
+        idx = torch.cat([torch.cat([torch.arange(s0, s0 + P), torch.arange(o0, o0 + r)])
+                         for (P, L), s0 in zip(groups, _group_starts(groups))
+                         for o0, r in zip(_resp_offsets(P, L, s0), L)]).to(dev)
+        rq, rk, rv, rd = (x.index_select(0, idx) for x in (q, k, v, do))
+        del q, k, v, do
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats(dev)
+        rgp = binding.GroupPacking([(0, rlen)])
+        log(f"[bench] replicated layout T={rgp.T}")
+        rt = run(rgp, rq, rk, rv, rd, max(2, args.steps // 2), 1)
+        rpeak = torch.cuda.max_memory_allocated(dev)
+        rep = {"ms_per_step": rt["ms_per_step"], "speedup_packed_over_replicated": rt["ms_per_step"] / ms,
+               "tokens": rgp.T, "peak_hbm_gb": rpeak / 1e9}
+        log(f"[bench] replicated: {rt['ms_per_step']:.2f} ms/step -> packed speed-up {rt['ms_per_step'] / ms:.2f}x")
+    line = {
+        "metric": "fwd+bwd useful TFLOP/s and % bf16 MFMA peak, several prompt groups per call",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic: seeded i.i.d. normal bf16 q/k/v/dO",
+        "frac_of_peak": value / PEAK_BF16_TFLOPS,
+        "config": {"workload": name, "groups": w.B, "P": w.P, "N": w.N, "R": w.R, "Hq": inp.Hq,
+                   "Hkv": inp.Hkv, "head_dim": inp.d, "packed_tokens": gp.T, "pairs_per_head": pairs,
+                   "useful_tflop_per_step": useful / 1e12, "parallelism": "single GPU"},
+        "timing_ms": {kk: round(vv, 4) for kk, vv in t.items()},
+        "roofline": {"bound": "mfma", "kernel": "fwd+bwd step (all kernels)",
+                     "achieved": executed / (ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": executed / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "traffic": None,
+                     "traffic_source": "no counters for this workload",
+                     "algorithmic_flop_per_step": executed},
+        "peak_hbm_gb": peak / 1e9, "replicated": rep, "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def _group_starts(groups):
+    s, out = 0, []
+    for P, L in groups:
+        out.append(s)
+        s += P + sum(L)
+    return out
+
+
+def _resp_offsets(P, L, start):
+    o, out = start + P, []
+    for r in L:
+        out.append(o)
+        o += r
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -227,13 +346,15 @@ def main() -> int:
     import torch
 
     from exact_shared_prefix_amd import binding, metrics
-    from exact_shared_prefix_amd.inputs import HEADLINE, WORKLOADS, workload_inputs
+    from exact_shared_prefix_amd.inputs import GROUP_WORKLOADS, HEADLINE, WORKLOADS, workload_inputs
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     binding.load()
     name = args.workload or HEADLINE
+    if name in GROUP_WORKLOADS:
+        return group_main(args, name)
     w = WORKLOADS[name]
     log(f"[bench] workload {name}: generating seeded inputs")
     inp = workload_inputs(w)

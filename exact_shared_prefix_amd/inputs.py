@@ -78,6 +78,52 @@ WORKLOADS = {
 HEADLINE = "rollout_p8k_r4k_n32"
 
 
+@dataclass(frozen=True)
+class GroupWorkload:
+    """Several shared-prompt groups packed back to back in one call: B groups
+    of P prompt tokens and N responses of R tokens each (Qwen3-8B heads)."""
+
+    name: str
+    B: int
+    P: int
+    R: int
+    N: int
+    Hq: int
+    Hkv: int
+    d: int
+    seed: int = 0
+    note: str = ""
+
+    @property
+    def groups(self) -> list:
+        return [(self.P, [self.R] * self.N) for _ in range(self.B)]
+
+    @property
+    def T(self) -> int:
+        return self.B * (self.P + self.N * self.R)
+
+
+GROUP_WORKLOADS = {
+    w.name: w
+    for w in [
+        GroupWorkload("microbatch_g8_p2k_r1k_n8", 8, 2048, 1024, 8, 32, 8, 128, 6,
+                      "8 prompt groups in one call, 81920 packed vs 196608 replicated tokens"),
+    ]
+}
+
+
+def group_workload_inputs(w: GroupWorkload | str) -> Inputs:
+    """Inputs of a multi-group workload: the [T, H, d] tensors are drawn like
+    a single packing of T rows (P = 0, one segment); the grouping is
+    w.groups."""
+    if isinstance(w, str):
+        w = GROUP_WORKLOADS[w]
+    inp = make_inputs(0, [w.T], w.Hq, w.Hkv, w.d, seed=w.seed)
+    inp.meta["workload"] = w.name
+    inp.meta["groups"] = w.groups
+    return inp
+
+
 def _threads() -> int:
     try:
         n = len(os.sched_getaffinity(0))
