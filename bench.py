@@ -321,6 +321,57 @@ def _resp_offsets(P, L, start):
     return out
 
 
+SWEEP_P = (1024, 4096, 16384)
+SWEEP_R = (256, 1024, 4096)
+SWEEP_N = (1, 2, 4, 8, 16, 32)
+
+
+def sweep_main(args) -> int:
+    """N / P / R sweep (Qwen3-8B heads): packed fwd+bwd time against the same
+    kernels on the replicated layout, the token compression
+    rho = N(P+R)/(P+NR) and the pair ratio, one JSON line per point and a
+    Markdown table on stderr. Where the packed layout stops paying off is
+    the row where the speed-up approaches 1."""
+    import torch
+
+    from exact_shared_prefix_amd import binding, metrics
+    from exact_shared_prefix_amd.inputs import make_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    Hq, Hkv, d = 32, 8, 128
+    rows = []
+    steps, warmup = max(2, args.steps // 3), 1
+    for P in SWEEP_P:
+        for R in SWEEP_R:
+            for N in SWEEP_N:
+                L = [R] * N
+                inp = make_inputs(P, L, Hq, Hkv, d, seed=7)
+                q, k, v, do = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.do))
+                t = time_steps(q, k, v, do, binding.Packing(P, L), inp.scale, steps, warmup, False)
+                rq, rk, rv, rd, rlen = replicated_inputs(q, k, v, do, P, L)
+                del q, k, v, do
+                rt = time_steps(rq, rk, rv, rd, binding.Packing(0, rlen), inp.scale, steps, warmup, False)
+                del rq, rk, rv, rd
+                torch.cuda.empty_cache()
+                packed_tok, rep_tok = metrics.tokens(P, L)
+                pairs = metrics.pairs(P, L)
+                rec = {"P": P, "R": R, "N": N, "packed_ms": t["ms_per_step"], "replicated_ms": rt["ms_per_step"],
+                       "speedup": rt["ms_per_step"] / t["ms_per_step"], "rho_tokens": rep_tok / packed_tok,
+                       "pair_ratio": metrics.replicated_pairs(P, L) / pairs,
+                       "useful_tflops": 14 * d * Hq * pairs / (t["ms_per_step"] * 1e-3) / 1e12}
+                rows.append(rec)
+                print(json.dumps(rec), flush=True)
+                log(f"[sweep] P={P} R={R} N={N}: packed {t['ms_per_step']:.2f} ms, replicated "
+                    f"{rt['ms_per_step']:.2f} ms, speed-up {rec['speedup']:.2f}x (pairs ratio {rec['pair_ratio']:.2f})")
+    log("| P | R | N | packed ms | replicated ms | speed-up | pair ratio | token ratio rho | useful TFLOP/s |")
+    log("|---|---|---|---|---|---|---|---|---|")
+    for r in rows:
+        log(f"| {r['P']} | {r['R']} | {r['N']} | {r['packed_ms']:.2f} | {r['replicated_ms']:.2f} | "
+            f"{r['speedup']:.2f} | {r['pair_ratio']:.2f} | {r['rho_tokens']:.2f} | {r['useful_tflops']:.0f} |")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -331,6 +382,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-mfma-peak", action="store_true", help="skip the measured MFMA peak")
+    ap.add_argument("--sweep", action="store_true",
+                    help="N/P/R sweep of packed vs replicated time (one JSON line per point)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -352,6 +405,8 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     binding.load()
+    if args.sweep:
+        return sweep_main(args)
     name = args.workload or HEADLINE
     if name in GROUP_WORKLOADS:
         return group_main(args, name)

@@ -83,6 +83,9 @@ SMALL = {
     "prompt_tail_empty_responses": dict(P=129, lengths=[0, 0, 31], Hq=2, Hkv=1, d=128, seed=25),
     "peaked_scores_q_x4": dict(P=160, lengths=[96, 33], Hq=4, Hkv=2, d=128, seed=26, qkv_scale=2.0),
     "ragged_d64_many": dict(P=70, lengths=[1, 2, 3, 130, 64, 65], Hq=4, Hkv=1, d=64, seed=27),
+    # small N with a long prompt and short responses (the sweep's crossover regime)
+    "small_n2_long_prompt": dict(P=1000, lengths=[37, 64], Hq=4, Hkv=2, d=128, seed=28),
+    "n1_prompt_only_response": dict(P=777, lengths=[1], Hq=2, Hkv=1, d=128, seed=29),
 }
 
 
