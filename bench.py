@@ -372,6 +372,64 @@ def sweep_main(args) -> int:
     return 0
 
 
+def layer_main(args) -> int:
+    """One packed decoder layer (Qwen3-8B shapes, random weights) at the
+    headline packing: fwd+bwd time on the P + sum(R) packed tokens against the
+    same layer on the N(P+R) replicated tokens; the ratio is the whole-layer
+    speed-up, to compare with the token ratio rho = N(P+R)/(P+NR)."""
+    import torch
+
+    from exact_shared_prefix_amd import binding, metrics
+    from exact_shared_prefix_amd.inputs import HEADLINE, WORKLOADS, response_lengths
+    from exact_shared_prefix_amd.layer import LayerConfig, init_weights, layer_forward, packed_positions
+
+    w = WORKLOADS[args.workload or HEADLINE]
+    P, L = w.P, response_lengths(w)
+    cfg = LayerConfig(Hq=w.Hq, Hkv=w.Hkv, d=w.d)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    weights = {k: t.requires_grad_(True) for k, t in init_weights(cfg, 8, dev).items()}
+
+    def run(pk, pos, steps, warmup):
+        g = torch.Generator(device=dev).manual_seed(9)
+        x = torch.randn(pk.T, cfg.hidden, device=dev, generator=g).to(torch.bfloat16).requires_grad_(True)
+        dy = torch.randn(pk.T, cfg.hidden, device=dev, generator=g).to(torch.bfloat16)
+        pos = pos.to(dev)
+        for _ in range(warmup):
+            layer_forward(x, weights, cfg, pk, pos).backward(dy)
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            layer_forward(x, weights, cfg, pk, pos).backward(dy)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps, torch.cuda.max_memory_allocated(dev)
+
+    steps, warmup = max(2, args.steps // 3), 1
+    pk = binding.Packing(P, L)
+    log(f"[layer] {w.name}: packed layer, T={pk.T}")
+    ms_p, mem_p = run(pk, packed_positions(P, L), steps, warmup)
+    log(f"[layer] packed: {ms_p:.1f} ms per fwd+bwd")
+    rlen = [P + r for r in L]
+    rpk = binding.Packing(0, rlen)
+    rpos = torch.cat([torch.arange(n) for n in rlen])
+    log(f"[layer] replicated layer, T={rpk.T}")
+    ms_r, mem_r = run(rpk, rpos, steps, warmup)
+    packed_tok, rep_tok = metrics.tokens(P, L)
+    rec = {"metric": "decoder layer fwd+bwd time, packed vs replicated tokens", "workload": w.name,
+           "layer": {"hidden": cfg.hidden, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "head_dim": cfg.d,
+                     "intermediate": cfg.inter},
+           "packed_ms": ms_p, "replicated_ms": ms_r, "speedup": ms_r / ms_p,
+           "rho_tokens": rep_tok / packed_tok, "packed_tokens": packed_tok, "replicated_tokens": rep_tok,
+           "peak_hbm_gb": {"packed": mem_p / 1e9, "replicated": mem_r / 1e9}, "steps": steps,
+           "note": "projections and MLP are library GEMMs (bf16); attention is this library's kernels"}
+    log(f"[layer] replicated: {ms_r:.1f} ms -> whole-layer speed-up {ms_r / ms_p:.2f}x (token ratio {rec['rho_tokens']:.2f})")
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -382,6 +440,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-mfma-peak", action="store_true", help="skip the measured MFMA peak")
+    ap.add_argument("--layer", action="store_true",
+                    help="one packed decoder layer (random weights) vs the replicated layout")
     ap.add_argument("--sweep", action="store_true",
                     help="N/P/R sweep of packed vs replicated time (one JSON line per point)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -407,6 +467,8 @@ def main() -> int:
     binding.load()
     if args.sweep:
         return sweep_main(args)
+    if args.layer:
+        return layer_main(args)
     name = args.workload or HEADLINE
     if name in GROUP_WORKLOADS:
         return group_main(args, name)

@@ -19,7 +19,9 @@ Two independent formulations of the same definition live here:
   the literal replication is too slow to run whole.
 
 ``groups`` extends both to several shared-prompt groups packed back to back
-(independent groups; each row attends only its own group).
+(independent groups; each row attends only its own group). ``layer`` is a
+float64 decoder layer run on the replicated sequences (for the packed-layer
+check).
 
 Every function in these modules has a pin in tests/test_oracle.py against
 something other than itself (library attention + autograd, closed forms,
@@ -28,3 +30,4 @@ finite differences, invariants).
 from .replicated import oracle_fwd_bwd, causal_attention_fwd, causal_attention_bwd  # noqa: F401
 from .sampled import attended_keys, rows_fwd_bwd, keys_dkdv  # noqa: F401
 from .groups import attended_keys_groups, group_starts, oracle_groups_fwd_bwd  # noqa: F401
+from .layer import layer64, replicated_layer, rms_norm64, rope64  # noqa: F401
