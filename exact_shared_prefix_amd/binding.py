@@ -20,7 +20,9 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 EXPORTS = ("dualkv_fwd_workspace_bytes", "dualkv_bwd_workspace_bytes", "dualkv_fwd",
            "dualkv_bwd", "dualkv_bwd_phases", "dualkv_status_string",
            "dualkv_fwd_workspace_bytes_groups", "dualkv_bwd_workspace_bytes_groups",
-           "dualkv_fwd_groups", "dualkv_bwd_groups")
+           "dualkv_fwd_groups", "dualkv_bwd_groups",
+           "dualkv_fwd_workspace_bytes_tree", "dualkv_bwd_workspace_bytes_tree",
+           "dualkv_fwd_tree", "dualkv_bwd_tree")
 PHASE_PRE, PHASE_MAIN, PHASE_FINISH, PHASE_DQ, PHASE_ALL = 1, 2, 4, 8, 15
 
 _lib = None
@@ -64,6 +66,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dualkv_fwd_groups.argtypes = [vp, vp, vp, vp, vp] + gargs + [c_float, vp, c_size, vp]
     lib.dualkv_bwd_groups.restype = c_int
     lib.dualkv_bwd_groups.argtypes = [vp] * 9 + gargs + [c_float, c_int, vp, c_size, vp]
+    targs = [c_int, i32p, i32p, c_int, c_int, c_int]
+    lib.dualkv_fwd_workspace_bytes_tree.restype = c_size
+    lib.dualkv_fwd_workspace_bytes_tree.argtypes = targs
+    lib.dualkv_bwd_workspace_bytes_tree.restype = c_size
+    lib.dualkv_bwd_workspace_bytes_tree.argtypes = targs + [c_int]
+    lib.dualkv_fwd_tree.restype = c_int
+    lib.dualkv_fwd_tree.argtypes = [vp, vp, vp, vp, vp] + targs + [c_float, vp, c_size, vp]
+    lib.dualkv_bwd_tree.restype = c_int
+    lib.dualkv_bwd_tree.argtypes = [vp] * 9 + targs + [c_float, c_int, vp, c_size, vp]
     lib.dualkv_status_string.restype = ctypes.c_char_p
     lib.dualkv_status_string.argtypes = [c_int]
     _lib = lib
@@ -124,6 +135,24 @@ class GroupPacking:
         i32p = ctypes.POINTER(ctypes.c_int32)
         return (self.B, ctypes.cast(self._P, i32p), ctypes.cast(self._N, i32p),
                 ctypes.cast(self._R, i32p))
+
+
+class TreePacking:
+    """Segments of a prefix forest in depth-first order: node_len[i] rows each,
+    node_parent[i] = parent segment (-1 for a root)."""
+
+    def __init__(self, node_len: Sequence[int], node_parent: Sequence[int]):
+        self.node_len = [int(x) for x in node_len]
+        self.node_parent = [int(x) for x in node_parent]
+        self.n = len(self.node_len)
+        self.T = sum(self.node_len)
+        self._len = (ctypes.c_int32 * max(1, self.n))(*self.node_len)
+        self._par = (ctypes.c_int32 * max(1, self.n))(*self.node_parent)
+        self._ws = {}
+
+    def args(self):
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        return (self.n, ctypes.cast(self._len, i32p), ctypes.cast(self._par, i32p))
 
 
 def _stream_ptr(stream) -> int:
@@ -285,6 +314,62 @@ def bwd_groups(q, k, v, o, lse, do, gp: GroupPacking, scale: Optional[float] = N
                                     _ptr(dq), _ptr(dk), _ptr(dv), *gp.args(), Hq, Hkv, d,
                                     float(scale), int(deterministic), _ptr(workspace),
                                     workspace.numel(), _stream_ptr(stream)))
+    return dq, dk, dv
+
+
+def fwd_tree(q, k, v, tp: TreePacking, scale: Optional[float] = None, out=None, lse=None,
+             workspace=None, stream=None):
+    """dualkv_fwd_tree -> (o, lse); layouts as fwd()."""
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    _check_tensor("q", q, (tp.T, Hq, d), torch.bfloat16, dev)
+    _check_tensor("k", k, (tp.T, Hkv, d), torch.bfloat16, dev)
+    _check_tensor("v", v, (tp.T, Hkv, d), torch.bfloat16, dev)
+    scale = d ** -0.5 if scale is None else scale
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((Hq, tp.T), dtype=torch.float32, device=dev) if lse is None else lse
+    _check_tensor("o", out, (tp.T, Hq, d), torch.bfloat16, dev)
+    _check_tensor("lse", lse, (Hq, tp.T), torch.float32, dev)
+    key = ("fwd", Hq, Hkv, d)
+    if key not in tp._ws:
+        tp._ws[key] = load().dualkv_fwd_workspace_bytes_tree(*tp.args(), Hq, Hkv, d)
+    nws = tp._ws[key]
+    if nws == 0:
+        raise DualKVError(ERR_INVALID_ARG, "invalid problem shape")
+    if workspace is None or workspace.numel() < nws:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+    _check(load().dualkv_fwd_tree(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), *tp.args(),
+                                  Hq, Hkv, d, float(scale), _ptr(workspace), workspace.numel(),
+                                  _stream_ptr(stream)))
+    return out, lse
+
+
+def bwd_tree(q, k, v, o, lse, do, tp: TreePacking, scale: Optional[float] = None,
+             dq=None, dk=None, dv=None, workspace=None, deterministic: bool = False, stream=None):
+    """dualkv_bwd_tree -> (dq, dk, dv); layouts as bwd()."""
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    for name, t, hh in (("q", q, Hq), ("o", o, Hq), ("do", do, Hq), ("k", k, Hkv), ("v", v, Hkv)):
+        _check_tensor(name, t, (tp.T, hh, d), torch.bfloat16, dev)
+    _check_tensor("lse", lse, (Hq, tp.T), torch.float32, dev)
+    scale = d ** -0.5 if scale is None else scale
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    key = ("bwd", Hq, Hkv, d, bool(deterministic))
+    if key not in tp._ws:
+        tp._ws[key] = load().dualkv_bwd_workspace_bytes_tree(*tp.args(), Hq, Hkv, d, int(deterministic))
+    nws = tp._ws[key]
+    if nws == 0:
+        raise DualKVError(ERR_INVALID_ARG, "invalid problem shape")
+    if workspace is None or workspace.numel() < nws:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+    _check(load().dualkv_bwd_tree(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                                  _ptr(dq), _ptr(dk), _ptr(dv), *tp.args(), Hq, Hkv, d,
+                                  float(scale), int(deterministic), _ptr(workspace),
+                                  workspace.numel(), _stream_ptr(stream)))
     return dq, dk, dv
 
 

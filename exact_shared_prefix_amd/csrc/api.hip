@@ -16,13 +16,15 @@
 
 namespace dkv {
 hipError_t launch_fwd(const Problem& pb, const void* q, const void* k, const void* vt, void* o,
-                      float* lse, const FwdItem* items_dev, int n_items, hipStream_t stream);
+                      float* lse, const FwdItem* items_dev, const Region* regions_dev, int n_items,
+                      int max_regions, hipStream_t stream);
 hipError_t launch_xpose_kv(const Problem& pb, const void* src, void* dst, const KeyBlock* blocks_dev,
                            int n_blocks, hipStream_t stream);
 hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dO, void* dQ, void* dK,
                       void* dV, const BwdItem* items_dev, int n_items, const FwdItem* qitems_dev,
-                      int n_qitems, float* delta, float* dk_acc, float* dv_acc, float* part,
+                      const Region* qregions_dev, int n_qitems, float* delta, float* dk_acc,
+                      float* dv_acc, float* part,
                       const int* tile_off, const int* tile_items, int n_tiles, hipStream_t stream,
                       int phase_mask);
 }  // namespace dkv
@@ -55,15 +57,11 @@ dualkv_status check_heads(long long T, int Hq, int Hkv, int d, Problem& pb) {
 }
 
 // One group given by P, N and uniform R or host offsets[N + 1] (offsets[0] == P,
-// non-decreasing), starting at row `start`. Appends it to pb.groups.
+// non-decreasing), starting at row `start`: a root segment (the prompt) with
+// one leaf per response. Appends them to pb.segs.
 dualkv_status add_group(int start, int P, int R, int N, const int32_t* offsets, Problem& pb,
                         long long& end) {
   if (P < 0 || N < 1) return DUALKV_ERR_INVALID_ARG;
-  Group gr;
-  gr.start = start;
-  gr.P = P;
-  gr.off.resize(N + 1);
-  long long o = (long long)start + P;
   if (offsets) {
     if (offsets[0] != P) return DUALKV_ERR_INVALID_ARG;
     for (int n = 0; n < N; ++n)
@@ -71,23 +69,37 @@ dualkv_status add_group(int start, int P, int R, int N, const int32_t* offsets, 
   } else if (R < 0) {
     return DUALKV_ERR_INVALID_ARG;
   }
+  std::vector<int> off(N + 1);
   for (int n = 0; n <= N; ++n) {
-    const long long on = offsets ? (long long)start + offsets[n] : o + (long long)n * R;
+    const long long on = offsets ? (long long)start + offsets[n] : (long long)start + P + (long long)n * R;
     if (on >= (1LL << 31)) return DUALKV_ERR_INVALID_ARG;
-    gr.off[n] = (int)on;
+    off[n] = (int)on;
   }
-  end = gr.off[N];
-  pb.groups.push_back(std::move(gr));
+  const int root = (int)pb.segs.size();
+  pb.segs.push_back({start, P, -1, 0});
+  for (int n = 0; n < N; ++n) pb.segs.push_back({off[n], off[n + 1] - off[n], root, 0});
+  end = off[N];
   return DUALKV_OK;
+}
+
+// subtree_end of every segment (segments are in depth-first order, so a
+// subtree is the segment and the run of later segments that descend from it)
+void finish_segments(Problem& pb) {
+  for (Segment& sg : pb.segs) sg.subtree_end = sg.start + sg.len;
+  for (int v = (int)pb.segs.size() - 1; v >= 0; --v) {
+    const int p = pb.segs[v].parent;
+    if (p >= 0) pb.segs[p].subtree_end = std::max(pb.segs[p].subtree_end, pb.segs[v].subtree_end);
+  }
 }
 
 // Single-group problem (the dualkv_fwd / dualkv_bwd arguments).
 dualkv_status check_shape(int P, int R, int N, const int32_t* offsets, int Hq, int Hkv, int d,
                           Problem& pb) {
-  pb.groups.clear();
+  pb.segs.clear();
   long long T = 0;
   const dualkv_status st = add_group(0, P, R, N, offsets, pb, T);
   if (st != DUALKV_OK) return st;
+  finish_segments(pb);
   return check_heads(T, Hq, Hkv, d, pb);
 }
 
@@ -96,7 +108,7 @@ dualkv_status check_shape(int P, int R, int N, const int32_t* offsets, int Hq, i
 // order (sum of group_N entries in all).
 dualkv_status check_groups(int B, const int32_t* group_P, const int32_t* group_N,
                            const int32_t* resp_len, int Hq, int Hkv, int d, Problem& pb) {
-  pb.groups.clear();
+  pb.segs.clear();
   if (B < 1 || !group_P || !group_N || !resp_len) return DUALKV_ERR_INVALID_ARG;
   long long start = 0;
   size_t r = 0;
@@ -116,6 +128,32 @@ dualkv_status check_groups(int B, const int32_t* group_P, const int32_t* group_N
     if (st != DUALKV_OK) return st;
     start = end;
   }
+  finish_segments(pb);
+  return check_heads(start, Hq, Hkv, d, pb);
+}
+
+// A forest of segments in depth-first order (the *_tree entry points): segment
+// i has node_len[i] rows (stored right after segment i - 1) and parent
+// node_parent[i], -1 for a root, else a segment on the path from a root to
+// segment i - 1 (depth-first order); at most kMaxRegions - 1 = 3 ancestors.
+dualkv_status check_tree(int n_nodes, const int32_t* node_len, const int32_t* node_parent, int Hq,
+                         int Hkv, int d, Problem& pb) {
+  pb.segs.clear();
+  if (n_nodes < 1 || !node_len || !node_parent) return DUALKV_ERR_INVALID_ARG;
+  std::vector<int> path;   // segments from the current root down to segment i - 1
+  long long start = 0;
+  for (int i = 0; i < n_nodes; ++i) {
+    const int par = node_parent[i];
+    if (node_len[i] < 0 || par < -1 || par >= i) return DUALKV_ERR_INVALID_ARG;
+    while (!path.empty() && path.back() != par) path.pop_back();
+    if (par >= 0 && path.empty()) return DUALKV_ERR_INVALID_ARG;   // parent not on the path
+    if ((int)path.size() >= kMaxRegions) return DUALKV_ERR_INVALID_ARG;
+    path.push_back(i);
+    pb.segs.push_back({(int)start, node_len[i], par, 0});
+    start += node_len[i];
+    if (start >= (1LL << 31)) return DUALKV_ERR_INVALID_ARG;
+  }
+  finish_segments(pb);
   return check_heads(start, Hq, Hkv, d, pb);
 }
 
@@ -174,56 +212,58 @@ hipError_t upload(void* dst, const void* src, size_t n, hipStream_t stream) {
   return staging->upload(dst, src, n, stream);
 }
 
-// 32-key blocks of the transposed K / V fragments, cut per region (each
-// group's prompt, then each of its responses). prompt_base[g] = first block of
-// group g's prompt, resp_base[g][n] = first block of its response n.
-std::vector<KeyBlock> key_blocks(const Problem& pb, std::vector<int>* prompt_base = nullptr,
-                                 std::vector<std::vector<int>>* resp_base = nullptr) {
+// 32-key blocks of the transposed K / V fragments, cut per segment;
+// base[v] = first block of segment v.
+std::vector<KeyBlock> key_blocks(const Problem& pb, std::vector<int>* base = nullptr) {
   std::vector<KeyBlock> blocks;
-  if (prompt_base) prompt_base->clear();
-  if (resp_base) resp_base->clear();
-  for (const Group& gr : pb.groups) {
-    if (prompt_base) prompt_base->push_back((int)blocks.size());
-    for (int kb = gr.start; kb < gr.start + gr.P; kb += 32) blocks.push_back({kb, gr.start + gr.P});
-    if (resp_base) resp_base->emplace_back();
-    for (int n = 0; n < gr.N(); ++n) {
-      const int a = gr.off[n], b = gr.off[n + 1];
-      if (resp_base) resp_base->back().push_back((int)blocks.size());
-      for (int kb = a; kb < b; kb += 32) blocks.push_back({kb, b});
-    }
+  if (base) base->clear();
+  for (const Segment& sg : pb.segs) {
+    if (base) base->push_back((int)blocks.size());
+    for (int kb = sg.start; kb < sg.start + sg.len; kb += 32) blocks.push_back({kb, sg.start + sg.len});
   }
   return blocks;
 }
 
-// Forward (and dQ) work list: query tiles of `rows` rows that never straddle
-// a segment, longest (most keys) first so the tail of the grid is short.
-std::vector<FwdItem> fwd_items(const Problem& pb, int rows = kFwdRows) {
-  std::vector<int> pbase;
-  std::vector<std::vector<int>> rbase;
-  key_blocks(pb, &pbase, &rbase);
-  std::vector<FwdItem> items;
-  for (size_t gi = 0; gi < pb.groups.size(); ++gi) {
-    const Group& gr = pb.groups[gi];
-    const int p0 = gr.start, p1 = gr.start + gr.P;
-    for (int r = p0; r < p1; r += rows) {
-      const int r1 = std::min(p1, r + rows);
-      items.push_back({r, r1, p0, r1, r1, pbase[gi], 0});
-    }
-    for (int n = 0; n < gr.N(); ++n) {
-      const int a = gr.off[n], b = gr.off[n + 1];
-      for (int r = a; r < b; r += rows)
-        items.push_back({r, std::min(b, r + rows), p0, p1, a, pbase[gi], rbase[gi][n]});
+// Forward (and dQ) work list: query tiles of `rows` rows of one segment, with
+// their key regions (ancestor segments root first, then the own segment up to
+// the tile's last row), longest (most keys) first so the tail of the grid is
+// short.
+std::vector<FwdItem> fwd_items(const Problem& pb, std::vector<Region>* regions, int rows = kFwdRows) {
+  std::vector<int> base;
+  key_blocks(pb, &base);
+  struct Tmp { FwdItem it; int keys; };
+  std::vector<Tmp> tmp;
+  std::vector<Region> regs;
+  std::vector<int> anc;
+  for (int v = 0; v < (int)pb.segs.size(); ++v) {
+    const Segment& sg = pb.segs[v];
+    anc.clear();
+    for (int a = sg.parent; a >= 0; a = pb.segs[a].parent) anc.push_back(a);
+    for (int r = sg.start; r < sg.start + sg.len; r += rows) {
+      const int r1 = std::min(sg.start + sg.len, r + rows);
+      const int off = (int)regs.size();
+      int keys = 0;
+      for (int x = (int)anc.size() - 1; x >= 0; --x) {
+        const Segment& as = pb.segs[anc[x]];
+        regs.push_back({as.start, as.start + as.len, base[anc[x]]});
+        keys += as.len;
+      }
+      regs.push_back({sg.start, r1, base[v]});
+      keys += r1 - sg.start;
+      tmp.push_back({{r, r1, off, (int)anc.size() + 1}, keys});
     }
   }
-  std::stable_sort(items.begin(), items.end(), [](const FwdItem& x, const FwdItem& y) {
-    return (x.a_end - x.a_start + x.r1 - x.b_start) > (y.a_end - y.a_start + y.r1 - y.b_start);
-  });
+  std::stable_sort(tmp.begin(), tmp.end(), [](const Tmp& x, const Tmp& y) { return x.keys > y.keys; });
+  std::vector<FwdItem> items;
+  for (const Tmp& t : tmp) items.push_back(t.it);
+  if (regions) *regions = std::move(regs);
   return items;
 }
 
-// dK/dV work list: kBwdKeys-key tiles, each paired with the rows that attend it
-// (all later rows of its group for a prompt tile, the later rows of its own
-// response for a response tile), cut on a fixed grid of kBwdChunk-row chunks.
+// dK/dV work list: kBwdKeys-key tiles of each segment, each paired with the
+// rows that attend it: the later rows of the segment's subtree (every later row
+// of its group for a prompt tile, the later rows of its own response for a
+// response tile), cut on a fixed grid of kBwdChunk-row chunks.
 // Items are ordered chunk-major so workgroups running together share query
 // rows. With tl_out != null, also returns each tile's items (ascending) as a
 // CSR list.
@@ -231,13 +271,9 @@ struct TileLists { std::vector<int> off, items; };
 std::vector<BwdItem> bwd_items(const Problem& pb, TileLists* tl_out = nullptr) {
   struct Tile { int kb, ke, rend; };
   std::vector<Tile> tiles;
-  for (const Group& gr : pb.groups) {
-    const int p1 = gr.start + gr.P;
-    for (int kb = gr.start; kb < p1; kb += kBwdKeys) tiles.push_back({kb, std::min(p1, kb + kBwdKeys), gr.end()});
-    for (int n = 0; n < gr.N(); ++n) {
-      const int a = gr.off[n], b = gr.off[n + 1];
-      for (int kb = a; kb < b; kb += kBwdKeys) tiles.push_back({kb, std::min(b, kb + kBwdKeys), b});
-    }
+  for (const Segment& sg : pb.segs) {
+    const int e = sg.start + sg.len;
+    for (int kb = sg.start; kb < e; kb += kBwdKeys) tiles.push_back({kb, std::min(e, kb + kBwdKeys), sg.subtree_end});
   }
   std::vector<BwdItem> items;
   std::vector<std::vector<int>> per_tile(tiles.size());
@@ -267,12 +303,13 @@ std::vector<BwdItem> bwd_items(const Problem& pb, TileLists* tl_out = nullptr) {
 // Forward workspace: work list, key blocks, V^T fragments
 // [block][Hkv][d/32][2][64][8] bf16.
 struct FwdLayout {
-  size_t items, blocks, vt, total;
+  size_t items, regions, blocks, vt, total;
 };
-FwdLayout fwd_layout(const Problem& pb, size_t n_items, size_t n_blocks) {
+FwdLayout fwd_layout(const Problem& pb, size_t n_items, size_t n_regions, size_t n_blocks) {
   FwdLayout L{};
   size_t off = 0;
-  L.items = off;  off = align_up(off + std::max<size_t>(1, n_items) * sizeof(FwdItem));
+  L.items = off;   off = align_up(off + std::max<size_t>(1, n_items) * sizeof(FwdItem));
+  L.regions = off; off = align_up(off + std::max<size_t>(1, n_regions) * sizeof(Region));
   L.blocks = off; off = align_up(off + std::max<size_t>(1, n_blocks) * sizeof(KeyBlock));
   L.vt = off;     off = align_up(off + n_blocks * pb.Hkv * (size_t)pb.d * 32 * sizeof(uint16_t));
   L.total = off;
@@ -280,17 +317,18 @@ FwdLayout fwd_layout(const Problem& pb, size_t n_items, size_t n_blocks) {
 }
 
 struct BwdLayout {
-  size_t items, qitems, delta, dk, dv, part, tile_off, tile_items, total;
+  size_t items, qitems, qregions, delta, dk, dv, part, tile_off, tile_items, total;
 };
 
 // Atomic mode: fp32 dK, dV accumulators [T][Hkv][d]. Deterministic mode:
 // per-item partials [n_items][Hkv][2][kBwdKeys][d] and the tile CSR lists.
-BwdLayout bwd_layout(const Problem& pb, size_t n_items, size_t n_qitems, bool det,
-                     size_t n_tiles) {
+BwdLayout bwd_layout(const Problem& pb, size_t n_items, size_t n_qitems, size_t n_qregions,
+                     bool det, size_t n_tiles) {
   BwdLayout L{};
   size_t off = 0;
-  L.items = off;  off = align_up(off + n_items * sizeof(BwdItem));
-  L.qitems = off; off = align_up(off + n_qitems * sizeof(FwdItem));
+  L.items = off;    off = align_up(off + n_items * sizeof(BwdItem));
+  L.qitems = off;   off = align_up(off + n_qitems * sizeof(FwdItem));
+  L.qregions = off; off = align_up(off + std::max<size_t>(1, n_qregions) * sizeof(Region));
   L.delta = off;  off = align_up(off + (size_t)pb.Hq * pb.T * sizeof(float));
   if (det) {
     L.part = off;       off = align_up(off + n_items * pb.Hkv * 2 * (size_t)kBwdKeys * pb.d * sizeof(float));
@@ -305,14 +343,18 @@ BwdLayout bwd_layout(const Problem& pb, size_t n_items, size_t n_qitems, bool de
 }
 
 size_t fwd_ws_bytes(const Problem& pb) {
-  return fwd_layout(pb, fwd_items(pb).size(), key_blocks(pb).size()).total;
+  std::vector<Region> regs;
+  const size_t ni = fwd_items(pb, &regs).size();
+  return fwd_layout(pb, ni, regs.size(), key_blocks(pb).size()).total;
 }
 
 size_t bwd_ws_bytes(const Problem& pb, bool det) {
   TileLists tl;
   const size_t ni = bwd_items(pb, &tl).size();
-  return bwd_layout(pb, std::max<size_t>(1, ni), std::max<size_t>(1, fwd_items(pb, kDqRows).size()),
-                    det, tl.off.size() - 1).total;
+  std::vector<Region> qregs;
+  const size_t nq = fwd_items(pb, &qregs, kDqRows).size();
+  return bwd_layout(pb, std::max<size_t>(1, ni), std::max<size_t>(1, nq), qregs.size(), det,
+                    tl.off.size() - 1).total;
 }
 
 dualkv_status fwd_impl(Problem& pb, const void* q, const void* k, const void* v, void* o,
@@ -322,22 +364,27 @@ dualkv_status fwd_impl(Problem& pb, const void* q, const void* k, const void* v,
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return DUALKV_ERR_INVALID_ARG;
   pb.scale = softmax_scale;
-  const std::vector<FwdItem> items = fwd_items(pb);
+  std::vector<Region> regs;
+  const std::vector<FwdItem> items = fwd_items(pb, &regs);
   const std::vector<KeyBlock> blocks = key_blocks(pb);
-  const FwdLayout L = fwd_layout(pb, items.size(), blocks.size());
+  const FwdLayout L = fwd_layout(pb, items.size(), regs.size(), blocks.size());
+  int max_regions = 1;
+  for (const FwdItem& it : items) max_regions = std::max(max_regions, it.n_reg);
   if (!workspace || workspace_bytes < L.total) return DUALKV_ERR_WORKSPACE;
   if (!aligned16(workspace)) return DUALKV_ERR_INVALID_ARG;
   if (items.empty()) return DUALKV_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   if (upload(ws + L.items, items.data(), items.size() * sizeof(FwdItem), s) != hipSuccess ||
+      upload(ws + L.regions, regs.data(), regs.size() * sizeof(Region), s) != hipSuccess ||
       (!blocks.empty() &&
        upload(ws + L.blocks, blocks.data(), blocks.size() * sizeof(KeyBlock), s) != hipSuccess))
     return DUALKV_ERR_HIP;
   if (launch_xpose_kv(pb, v, ws + L.vt, reinterpret_cast<const KeyBlock*>(ws + L.blocks),
                       (int)blocks.size(), s) != hipSuccess ||
       launch_fwd(pb, q, k, ws + L.vt, o, lse, reinterpret_cast<const FwdItem*>(ws + L.items),
-                 (int)items.size(), s) != hipSuccess)
+                 reinterpret_cast<const Region*>(ws + L.regions), (int)items.size(), max_regions,
+                 s) != hipSuccess)
     return DUALKV_ERR_HIP;
   return DUALKV_OK;
 }
@@ -355,10 +402,11 @@ dualkv_status bwd_impl(Problem& pb, const void* q, const void* k, const void* v,
   const bool det = deterministic != 0;
   TileLists tl;
   const std::vector<BwdItem> items = bwd_items(pb, &tl);
-  const std::vector<FwdItem> qitems = fwd_items(pb, kDqRows);
+  std::vector<Region> qregs;
+  const std::vector<FwdItem> qitems = fwd_items(pb, &qregs, kDqRows);
   const int n_tiles = (int)tl.off.size() - 1;
   const BwdLayout L = bwd_layout(pb, std::max<size_t>(1, items.size()),
-                                 std::max<size_t>(1, qitems.size()), det, n_tiles);
+                                 std::max<size_t>(1, qitems.size()), qregs.size(), det, n_tiles);
   if (!workspace || workspace_bytes < L.total) return DUALKV_ERR_WORKSPACE;
   if (!aligned16(workspace)) return DUALKV_ERR_INVALID_ARG;
   if (pb.T == 0) return DUALKV_OK;
@@ -374,11 +422,13 @@ dualkv_status bwd_impl(Problem& pb, const void* q, const void* k, const void* v,
        upload(ws + L.tile_items, tl.items.data(), tl.items.size() * sizeof(int), s) != hipSuccess))
     return DUALKV_ERR_HIP;
   if ((phase_mask & 8) && !qitems.empty() &&
-      upload(ws + L.qitems, qitems.data(), qitems.size() * sizeof(FwdItem), s) != hipSuccess)
+      (upload(ws + L.qitems, qitems.data(), qitems.size() * sizeof(FwdItem), s) != hipSuccess ||
+       upload(ws + L.qregions, qregs.data(), qregs.size() * sizeof(Region), s) != hipSuccess))
     return DUALKV_ERR_HIP;
   if (launch_bwd(pb, q, k, v, o, lse, dO, dQ, dK, dV, reinterpret_cast<const BwdItem*>(ws + L.items),
                  (int)items.size(), reinterpret_cast<const FwdItem*>(ws + L.qitems),
-                 (int)qitems.size(), reinterpret_cast<float*>(ws + L.delta),
+                 reinterpret_cast<const Region*>(ws + L.qregions), (int)qitems.size(),
+                 reinterpret_cast<float*>(ws + L.delta),
                  det ? nullptr : reinterpret_cast<float*>(ws + L.dk),
                  det ? nullptr : reinterpret_cast<float*>(ws + L.dv),
                  det ? reinterpret_cast<float*>(ws + L.part) : nullptr,
@@ -486,6 +536,43 @@ const char* dualkv_status_string(dualkv_status s) {
     case DUALKV_ERR_HIP: return "HIP runtime or kernel launch error";
   }
   return "unknown status";
+}
+
+size_t dualkv_fwd_workspace_bytes_tree(int n_nodes, const int32_t* node_len,
+                                       const int32_t* node_parent, int Hq, int Hkv, int d) {
+  Problem pb;
+  if (check_tree(n_nodes, node_len, node_parent, Hq, Hkv, d, pb) != DUALKV_OK) return 0;
+  return fwd_ws_bytes(pb);
+}
+
+size_t dualkv_bwd_workspace_bytes_tree(int n_nodes, const int32_t* node_len,
+                                       const int32_t* node_parent, int Hq, int Hkv, int d,
+                                       int deterministic) {
+  Problem pb;
+  if (check_tree(n_nodes, node_len, node_parent, Hq, Hkv, d, pb) != DUALKV_OK) return 0;
+  return bwd_ws_bytes(pb, deterministic != 0);
+}
+
+dualkv_status dualkv_fwd_tree(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int n_nodes, const int32_t* node_len, const int32_t* node_parent,
+                              int Hq, int Hkv, int d, float softmax_scale, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  Problem pb;
+  const dualkv_status st = check_tree(n_nodes, node_len, node_parent, Hq, Hkv, d, pb);
+  if (st != DUALKV_OK) return st;
+  return fwd_impl(pb, q, k, v, o, lse, softmax_scale, workspace, workspace_bytes, stream);
+}
+
+dualkv_status dualkv_bwd_tree(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dO, void* dQ, void* dK, void* dV,
+                              int n_nodes, const int32_t* node_len, const int32_t* node_parent,
+                              int Hq, int Hkv, int d, float softmax_scale, int deterministic,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  Problem pb;
+  const dualkv_status st = check_tree(n_nodes, node_len, node_parent, Hq, Hkv, d, pb);
+  if (st != DUALKV_OK) return st;
+  return bwd_impl(pb, q, k, v, o, lse, dO, dQ, dK, dV, softmax_scale, deterministic, workspace,
+                  workspace_bytes, stream, 15);
 }
 
 }  // extern "C"

@@ -322,8 +322,8 @@ template <int D>
 __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const u16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
-    u16* __restrict__ dQ, const FwdItem* __restrict__ items, HeadMap hm, int T, int Hq, int Hkv,
-    float c, float scale) {
+    u16* __restrict__ dQ, const FwdItem* __restrict__ items, const Region* __restrict__ regions,
+    HeadMap hm, int T, int Hq, int Hkv, float c, float scale) {
   constexpr int NW = kDqWaves;
   constexpr int BK = 64;          // keys per tile
   constexpr int NKK = D / 16;
@@ -376,13 +376,35 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) dqacc[dt] = f32x16{};
 
-  const int nA = (it.a_end - it.a_start + BK - 1) / BK;
-  const int nB = it.r1 > it.b_start ? (it.r1 - it.b_start + BK - 1) / BK : 0;
-  const int ntiles = nA + nB;
-  auto tile_bounds = [&](int i, int& kb, int& ke) {
-    if (i < nA) { kb = it.a_start + i * BK; ke = it.a_end; }
-    else { kb = it.b_start + (i - nA) * BK; ke = it.r1; }
+  // key regions of the item (ancestor segments, then its own up to r1), kept in
+  // scalar registers; tile i of the item is tile i - tbeg[x] of region x
+  int rk0[kMaxRegions], rk1[kMaxRegions], rblk[kMaxRegions], tbeg[kMaxRegions + 1];
+  tbeg[0] = 0;
+#pragma unroll
+  for (int x = 0; x < kMaxRegions; ++x) {
+    const Region rg = x < it.n_reg ? regions[it.reg_off + x] : Region{0, 0, 0};
+    rk0[x] = rg.k0;
+    rk1[x] = rg.k1;
+    rblk[x] = rg.blk;
+    tbeg[x + 1] = tbeg[x] + (rg.k1 - rg.k0 + BK - 1) / BK;
+  }
+  const int ntiles = tbeg[kMaxRegions];
+  // tile i: keys [kb, ke) of its region (ke = region end), b0 = its first block
+  auto tile_region = [&](int i, int& kb, int& ke, int& b0) __attribute__((always_inline)) {
+    kb = 0; ke = 0; b0 = 0;
+#pragma unroll
+    for (int x = 0; x < kMaxRegions; ++x)
+      if (i >= tbeg[x] && i < tbeg[x + 1]) {
+        kb = rk0[x] + (i - tbeg[x]) * BK;
+        ke = rk1[x];
+        b0 = rblk[x] + (i - tbeg[x]) * (BK / 32);
+      }
   };
+  auto tile_bounds = [&](int i, int& kb, int& ke) __attribute__((always_inline)) {
+    int b0;
+    tile_region(i, kb, ke, b0);
+  };
+
   // copies of tile i: job f = w, w + NW, ...: tensor f / NTF, key block
   // (f / NKK) % 2, d chunk f % NKK; keys past the region end read its last key
   auto stage = [&](int i, u16* ka, u16* va) {
@@ -499,7 +521,7 @@ static int stream_grid(size_t n4) {
 hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dO, void* dQ, void* dK,
                       void* dV, const BwdItem* items_dev, int n_items, const FwdItem* qitems_dev,
-                      int n_qitems, float* delta, float* dk_acc, float* dv_acc, float* part,
+                      const Region* qregions_dev, int n_qitems, float* delta, float* dk_acc, float* dv_acc, float* part,
                       const int* tile_off, const int* tile_items, int n_tiles, hipStream_t stream,
                       int phase_mask) {
   const size_t nk = (size_t)pb.T * pb.Hkv * pb.d;
@@ -541,12 +563,12 @@ hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const voi
     dim3 grid(headmap_grid(hm)), block(64 * kDqWaves);
     if (pb.d == 128)
       hipLaunchKernelGGL((dq_kernel<128>), grid, block, 0, stream, (const u16*)q, (const u16*)k,
-                         (const u16*)v, (const u16*)dO, lse, delta, (u16*)dQ, qitems_dev, hm, pb.T,
-                         pb.Hq, pb.Hkv, c, pb.scale);
+                         (const u16*)v, (const u16*)dO, lse, delta, (u16*)dQ, qitems_dev,
+                         qregions_dev, hm, pb.T, pb.Hq, pb.Hkv, c, pb.scale);
     else
       hipLaunchKernelGGL((dq_kernel<64>), grid, block, 0, stream, (const u16*)q, (const u16*)k,
-                         (const u16*)v, (const u16*)dO, lse, delta, (u16*)dQ, qitems_dev, hm, pb.T,
-                         pb.Hq, pb.Hkv, c, pb.scale);
+                         (const u16*)v, (const u16*)dO, lse, delta, (u16*)dQ, qitems_dev,
+                         qregions_dev, hm, pb.T, pb.Hq, pb.Hkv, c, pb.scale);
   }
   // 4. dK, dV to bf16: convert the accumulators, or reduce the partials in order
   if (phase_mask & 4) {

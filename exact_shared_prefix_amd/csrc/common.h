@@ -21,29 +21,29 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // ---------------------------------------------------------------- problem --
-// Host-side description of one packed micro-batch: one or more shared-prompt
-// groups stored back to back. Group g's prompt is rows [start, start + P) and
-// its response n is rows [off[n], off[n + 1]) (off[0] = start + P).
-struct Group {
-  int start = 0, P = 0;
-  std::vector<int> off;
-  int N() const { return (int)off.size() - 1; }
-  int end() const { return off.back(); }
-};
+// Host-side description of one packed micro-batch as a forest of segments in
+// depth-first order: segment v is rows [start, start + len), and a row of v
+// attends every key of v's proper ancestors plus the keys of v up to itself.
+// One shared-prompt group is a root (the prompt) with one leaf per response;
+// several groups are several such trees; deeper trees are multi-level shared
+// prefixes. subtree_end = end of the last row of v's subtree.
+struct Segment { int start = 0, len = 0, parent = -1, subtree_end = 0; };
 struct Problem {
   int T = 0;          // packed tokens
   int Hq = 0, Hkv = 0, G = 0, d = 0;
   float scale = 0.f;  // softmax scale
-  std::vector<Group> groups;
+  std::vector<Segment> segs;
 };
+constexpr int kMaxRegions = 4;   // key regions of a row: at most 3 ancestors + its own segment
 
-// Forward work item: query rows [r0, r1) of one segment; KV region A is
-// [a_start, a_end) (the group's prompt, or its prompt rows up to r1 for a
-// prompt tile) and region B is [b_start, r1) (the own response; empty for a
-// prompt tile). a_blk, b_blk are the indices of the regions' first 32-key
-// blocks in the transposed fragment layout (blocks are cut per region: each
-// prompt's, each response's, so a region's tiles start on a block).
-struct FwdItem { int r0, r1, a_start, a_end, b_start, a_blk, b_blk; };
+// Forward work item: query rows [r0, r1) of one segment; its key regions are
+// regions[reg_off .. reg_off + n_reg): the ancestors' whole segments, root
+// first, then its own segment up to r1 (causal there).
+struct FwdItem { int r0, r1, reg_off, n_reg; };
+// Key region [k0, k1); blk = index of its first 32-key block in the
+// transposed fragment layout (blocks are cut per segment, so every 64-key tile
+// of a region starts on a block).
+struct Region { int k0, k1, blk; };
 
 // 32-key block of the transposed fragment layout: keys [key0, key0 + 32)
 // clamped to [key0, kend) (kend = end of the block's region).

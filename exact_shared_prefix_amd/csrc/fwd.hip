@@ -65,12 +65,14 @@ __global__ __launch_bounds__(256) void xpose_kv_kernel(const u16* __restrict__ s
 }
 
 // ZERO_SCALE: the softmax scale is 0, so a masked score (-inf) times the scale
-// is not -inf and masked probabilities are zeroed explicitly
-template <int D, bool ZERO_SCALE>
+// is not -inf and masked probabilities are zeroed explicitly. NR: the most key
+// regions any item has (2 for one prompt level, up to kMaxRegions).
+template <int D, bool ZERO_SCALE, int NR>
 __global__ __launch_bounds__(64 * kFwdWaves, 1) void fwd_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ vt,
     u16* __restrict__ o, float* __restrict__ lse, const FwdItem* __restrict__ items,
-    HeadMap hm, int T, int Hq, int Hkv, float c /* softmax scale * log2(e) */) {
+    const Region* __restrict__ regions, HeadMap hm, int T, int Hq, int Hkv,
+    float c /* softmax scale * log2(e) */) {
   constexpr int NW = kFwdWaves;
   constexpr int BK = 64;          // keys per tile
   constexpr int NKK = D / 16;
@@ -124,13 +126,36 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void fwd_kernel(
   f32x16 s[2];        // S^T of the current tile: block kb2, register r <-> key kb + 32 kb2 + 8 (r/4) + 4 hl + r%4
   bf16x8 pf[2][2];    // P^T of the previous tile, B operands of O^T += V^T P^T
 
-  const int nA = (it.a_end - it.a_start + BK - 1) / BK;
-  const int nB = it.r1 > it.b_start ? (it.r1 - it.b_start + BK - 1) / BK : 0;
-  const int n = nA + nB;
-  auto tile_bounds = [&](int i, int& kb, int& ke) __attribute__((always_inline)) {
-    if (i < nA) { kb = it.a_start + i * BK; ke = it.a_end; }
-    else { kb = it.b_start + (i - nA) * BK; ke = it.r1; }
+  // key regions of the item (ancestor segments, then its own up to r1), kept in
+  // scalar registers; tile i of the item is tile i - tbeg[x] of region x
+  static_assert(NR >= 1 && NR <= kMaxRegions, "region count");
+  int rk0[NR], rk1[NR], rblk[NR], tbeg[NR + 1];
+  tbeg[0] = 0;
+#pragma unroll
+  for (int x = 0; x < NR; ++x) {
+    const Region rg = x < it.n_reg ? regions[it.reg_off + x] : Region{0, 0, 0};
+    rk0[x] = rg.k0;
+    rk1[x] = rg.k1;
+    rblk[x] = rg.blk;
+    tbeg[x + 1] = tbeg[x] + (rg.k1 - rg.k0 + BK - 1) / BK;
+  }
+  const int n = tbeg[NR];
+  // tile i: keys [kb, ke) of its region (ke = region end), b0 = its first block
+  auto tile_region = [&](int i, int& kb, int& ke, int& b0) __attribute__((always_inline)) {
+    kb = 0; ke = 0; b0 = 0;
+#pragma unroll
+    for (int x = 0; x < NR; ++x)
+      if (i >= tbeg[x] && i < tbeg[x + 1]) {
+        kb = rk0[x] + (i - tbeg[x]) * BK;
+        ke = rk1[x];
+        b0 = rblk[x] + (i - tbeg[x]) * (BK / 32);
+      }
   };
+  auto tile_bounds = [&](int i, int& kb, int& ke) __attribute__((always_inline)) {
+    int b0;
+    tile_region(i, kb, ke, b0);
+  };
+
   // copies of tile i by the trailing waves (copy f = (w - NL) + NL j):
   // K: key block f / NKK, d chunk f % NKK, keys past the region end read its
   // last key; V^T: block f / (2 NDT) of the tile (clamped to the last block
@@ -148,9 +173,8 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void fwd_kernel(
     }
   };
   auto copy_vt = [&](int i, u16* dst) __attribute__((always_inline)) {
-    int kb, ke;
-    tile_bounds(i, kb, ke);
-    const int b0 = i < nA ? it.a_blk + (kb - it.a_start) / 32 : it.b_blk + (kb - it.b_start) / 32;
+    int kb, ke, b0;
+    tile_region(i, kb, ke, b0);
     const int blast = b0 + (ke - 1 - kb) / 32;
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
@@ -303,15 +327,19 @@ hipError_t launch_xpose_kv(const Problem& pb, const void* src, void* dst, const 
 }
 
 hipError_t launch_fwd(const Problem& pb, const void* q, const void* k, const void* vt, void* o,
-                      float* lse, const FwdItem* items_dev, int n_items, hipStream_t stream) {
+                      float* lse, const FwdItem* items_dev, const Region* regions_dev, int n_items,
+                      int max_regions, hipStream_t stream) {
   if (n_items == 0) return hipSuccess;
   HeadMap hm = make_headmap(n_items, pb.Hq);
   dim3 grid(headmap_grid(hm)), block(64 * kFwdWaves);
   const float c = pb.scale * kLog2e;
-  auto kern = pb.d == 128 ? (c == 0.f ? fwd_kernel<128, true> : fwd_kernel<128, false>)
-                          : (c == 0.f ? fwd_kernel<64, true> : fwd_kernel<64, false>);
+  const bool z = c == 0.f, deep = max_regions > 2;
+  auto kern = pb.d == 128 ? (deep ? (z ? fwd_kernel<128, true, kMaxRegions> : fwd_kernel<128, false, kMaxRegions>)
+                                  : (z ? fwd_kernel<128, true, 2> : fwd_kernel<128, false, 2>))
+                          : (deep ? (z ? fwd_kernel<64, true, kMaxRegions> : fwd_kernel<64, false, kMaxRegions>)
+                                  : (z ? fwd_kernel<64, true, 2> : fwd_kernel<64, false, 2>));
   hipLaunchKernelGGL(kern, grid, block, 0, stream, (const u16*)q, (const u16*)k, (const u16*)vt,
-                     (u16*)o, lse, items_dev, hm, pb.T, pb.Hq, pb.Hkv, c);
+                     (u16*)o, lse, items_dev, regions_dev, hm, pb.T, pb.Hq, pb.Hkv, c);
   return hipGetLastError();
 }
 

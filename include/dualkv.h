@@ -151,6 +151,35 @@ dualkv_status dualkv_bwd_groups(const void* q, const void* k, const void* v, con
                                 float softmax_scale, int deterministic, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* Multi-level shared prefixes. The DualKV summary page names, as a limitation,
+ * that only one shared prefix per group is handled and tree-structured
+ * prefixes are not ("Limitations"). Here the packed rows form a forest of
+ * segments stored in depth-first order: segment i holds node_len[i] rows,
+ * right after segment i - 1 (segment 0 starts at row 0), and its parent is
+ * node_parent[i] (-1 for a root; otherwise a segment on the path from the
+ * current root to segment i - 1, so every subtree is a contiguous run of
+ * rows). A row of segment v attends every key of v's proper ancestors and the
+ * keys of v up to itself (causal). One shared-prompt group is a root prompt
+ * with one leaf per response, so the single- and multi-group entry points are
+ * special cases. At most 3 ancestors per segment (4 levels); node_len >= 0;
+ * HOST int32 arrays of n_nodes >= 1 entries; anything else, or a parent that
+ * breaks the depth-first order, is DUALKV_ERR_INVALID_ARG. Every other
+ * convention is that of the single-group entry points. */
+size_t dualkv_fwd_workspace_bytes_tree(int n_nodes, const int32_t* node_len,
+                                       const int32_t* node_parent, int Hq, int Hkv, int d);
+size_t dualkv_bwd_workspace_bytes_tree(int n_nodes, const int32_t* node_len,
+                                       const int32_t* node_parent, int Hq, int Hkv, int d,
+                                       int deterministic);
+dualkv_status dualkv_fwd_tree(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int n_nodes, const int32_t* node_len, const int32_t* node_parent,
+                              int Hq, int Hkv, int d, float softmax_scale, void* workspace,
+                              size_t workspace_bytes, void* stream);
+dualkv_status dualkv_bwd_tree(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dO, void* dQ, void* dK, void* dV,
+                              int n_nodes, const int32_t* node_len, const int32_t* node_parent,
+                              int Hq, int Hkv, int d, float softmax_scale, int deterministic,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static English description of a status code (never NULL). */
 const char* dualkv_status_string(dualkv_status s);
 

@@ -21,7 +21,8 @@ Two independent formulations of the same definition live here:
 ``groups`` extends both to several shared-prompt groups packed back to back
 (independent groups; each row attends only its own group). ``layer`` is a
 float64 decoder layer run on the replicated sequences (for the packed-layer
-check).
+check); ``tree`` runs every root-to-leaf path of a multi-level prefix forest
+as its own causal sequence.
 
 Every function in these modules has a pin in tests/test_oracle.py against
 something other than itself (library attention + autograd, closed forms,
@@ -31,3 +32,4 @@ from .replicated import oracle_fwd_bwd, causal_attention_fwd, causal_attention_b
 from .sampled import attended_keys, rows_fwd_bwd, keys_dkdv  # noqa: F401
 from .groups import attended_keys_groups, group_starts, oracle_groups_fwd_bwd  # noqa: F401
 from .layer import layer64, replicated_layer, rms_norm64, rope64  # noqa: F401
+from .tree import attended_keys_tree, leaf_paths, oracle_tree_fwd_bwd, segment_starts  # noqa: F401

@@ -190,6 +190,38 @@ def test_group_workspace_sizes(lib):
     assert lib.dualkv_fwd_workspace_bytes_groups(0, _arr((16,)), _arr((3,)), _arr((8,)), 4, 2, 128) == 0
 
 
+def _fwd_tree(lib, lens=(8, 4, 3, 5), par=(-1, 0, 1, 0), Hq=4, Hkv=2, d=128, ws_bytes=1 << 20):
+    return lib.dualkv_fwd_tree(FAKE, FAKE, FAKE, FAKE, FAKE, len(lens) if lens else 0, _arr(lens),
+                               _arr(par), Hq, Hkv, d, 0.1, FAKE, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lens=()), ERR_INVALID_ARG),
+    (dict(par=(-1, 0, 2, 0)), ERR_INVALID_ARG),          # parent not before the segment
+    (dict(par=(-1, 0, 1, 2), lens=(8, 4, 3, 5)), OK),    # a chain is fine (checked below with ws)
+    (dict(lens=(8, 4, 3, 5, 2), par=(-1, 0, 1, 0, 2)), ERR_INVALID_ARG),   # 2 left the path at 3
+    (dict(lens=(8, 4, -3, 5)), ERR_INVALID_ARG),
+    (dict(lens=(1, 1, 1, 1, 1), par=(-1, 0, 1, 2, 3)), ERR_INVALID_ARG),   # 4 ancestors
+    (dict(d=96), ERR_UNSUPPORTED),
+    (dict(ws_bytes=16), ERR_WORKSPACE),
+])
+def test_fwd_tree_rejects_bad_arguments(lib, kw, status):
+    if status == OK:
+        kw = dict(kw, ws_bytes=16)
+        status = ERR_WORKSPACE   # shape accepted, then the workspace check fails
+    assert _fwd_tree(lib, **kw) == status
+
+
+def test_tree_workspace_matches_single_group(lib):
+    # root prompt + leaves is the single-group problem
+    for det in (0, 1):
+        t = lib.dualkv_bwd_workspace_bytes_tree(4, _arr((16, 8, 0, 5)), _arr((-1, 0, 0, 0)), 4, 2, 128, det)
+        g = lib.dualkv_bwd_workspace_bytes(16, 0, 3, _arr((16, 24, 24, 29)), 4, 2, 128, det)
+        assert t == g > 0
+    t = lib.dualkv_fwd_workspace_bytes_tree(4, _arr((16, 8, 0, 5)), _arr((-1, 0, 0, 0)), 4, 2, 128)
+    assert t == lib.dualkv_fwd_workspace_bytes(16, 0, 3, _arr((16, 24, 24, 29)), 4, 2, 128) > 0
+
+
 def test_pair_accounting_matches_brute_force():
     from oracle import attended_keys
     for P, lengths in ((5, [3, 0, 4]), (0, [6, 2]), (9, [1])):

@@ -426,3 +426,87 @@ def test_group_attended_keys_against_independent_definition():
     groups = [(3, [2, 0, 1]), (0, [4]), (5, [2])]
     for t in range(group_starts(groups)[-1]):
         assert list(attended_keys_groups(t, groups)) == _groups_attended(t, groups)
+
+
+# ------------------------------------------------- multi-level prefix trees --
+from oracle import attended_keys_tree, oracle_tree_fwd_bwd, segment_starts  # noqa: E402
+
+
+def _tree_attended(t, node_len, node_parent):
+    """A(t) written out independently: walk the segments to find row t's, then
+    list the keys of every ancestor (root first) and its own up to t."""
+    start = 0
+    for v, n in enumerate(node_len):
+        if start <= t < start + n:
+            break
+        start += n
+    else:
+        raise IndexError(t)
+    starts = [sum(node_len[:i]) for i in range(len(node_len))]
+    chain = []
+    a = node_parent[v]
+    while a != -1:
+        chain.insert(0, a)
+        a = node_parent[a]
+    keys = []
+    for a in chain:
+        keys += list(range(starts[a], starts[a] + node_len[a]))
+    return keys + list(range(starts[v], t + 1))
+
+
+TREE_CASES = [
+    # (node_len, node_parent, Hq, Hkv, d): depth-first order
+    ([4, 3, 2, 0, 3, 5, 2, 3], [-1, 0, 1, 1, 0, -1, 5, 5], 4, 2, 8),
+    ([3, 2, 2, 1, 4], [-1, 0, 1, 2, 0], 2, 1, 4),   # a chain of four levels and a sibling
+]
+
+
+def _tree_mask_reference(q, k, v, do, node_len, node_parent, scale):
+    T = sum(node_len)
+    groups_like = None  # noqa: F841
+    Hq, Hkv = q.shape[1], k.shape[1]
+    G = Hq // Hkv
+    M = torch.zeros(T, T, dtype=torch.bool)
+    for t in range(T):
+        M[t, _tree_attended(t, node_len, node_parent)] = True
+    qt = torch.tensor(q, dtype=torch.float64, requires_grad=True)
+    kt = torch.tensor(k, dtype=torch.float64, requires_grad=True)
+    vt = torch.tensor(v, dtype=torch.float64, requires_grad=True)
+    O = torch.zeros(T, Hq, q.shape[2], dtype=torch.float64)
+    LSE = torch.zeros(Hq, T, dtype=torch.float64)
+    for h in range(Hq):
+        S = (scale * (qt[:, h] @ kt[:, h // G].T)).masked_fill(~M, float("-inf"))
+        LSE[h] = torch.logsumexp(S, dim=1)
+        O[:, h] = torch.softmax(S, dim=1) @ vt[:, h // G]
+    (O * torch.tensor(do, dtype=torch.float64)).sum().backward()
+    return {"O": O.detach().numpy(), "LSE": LSE.detach().numpy(), "dQ": qt.grad.numpy(),
+            "dK": kt.grad.numpy(), "dV": vt.grad.numpy()}
+
+
+@pytest.mark.parametrize("case", range(len(TREE_CASES)))
+def test_tree_oracle_matches_dense_masked_attention(case):
+    node_len, node_parent, Hq, Hkv, d = TREE_CASES[case]
+    T = segment_starts(node_len)[-1]
+    rng = np.random.default_rng(70 + case)
+    q, do = rng.standard_normal((T, Hq, d)), rng.standard_normal((T, Hq, d))
+    k, v = rng.standard_normal((T, Hkv, d)), rng.standard_normal((T, Hkv, d))
+    got = oracle_tree_fwd_bwd(q, k, v, do, node_len, node_parent, 0.6)
+    ref = _tree_mask_reference(q, k, v, do, node_len, node_parent, 0.6)
+    for key in ("O", "LSE", "dQ", "dK", "dV"):
+        assert np.max(np.abs(got[key] - ref[key])) <= 1e-10, key
+
+
+def test_one_level_tree_is_the_single_group_oracle():
+    P, L = 6, [3, 0, 5]
+    inp = make_inputs(P, L, 4, 2, 8, seed=71)
+    q, k, v, do = _inputs_np(inp)
+    a = oracle_tree_fwd_bwd(q, k, v, do, [P] + L, [-1] + [0] * len(L), inp.scale)
+    b = oracle_fwd_bwd(q, k, v, do, P, L, inp.scale)
+    for key in ("O", "LSE", "dQ", "dK", "dV"):
+        assert np.max(np.abs(a[key] - b[key])) <= 1e-12, key
+
+
+def test_tree_attended_keys_against_independent_definition():
+    for node_len, node_parent, *_ in TREE_CASES:
+        for t in range(sum(node_len)):
+            assert list(attended_keys_tree(t, node_len, node_parent)) == _tree_attended(t, node_len, node_parent)

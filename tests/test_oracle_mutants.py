@@ -21,6 +21,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 REPLICATED = os.path.join(ROOT, "oracle", "replicated.py")
 SAMPLED = os.path.join(ROOT, "oracle", "sampled.py")
 GROUPS = os.path.join(ROOT, "oracle", "groups.py")
+TREE = os.path.join(ROOT, "oracle", "tree.py")
 
 
 def _load(path, old=None, new=None, nth=1, inject=None):
@@ -63,11 +64,15 @@ def _pin_calls():
         (pins.test_group_oracle_one_group_is_the_single_group_oracle, ()),
         (pins.test_groups_are_isolated, ()),
         (pins.test_group_attended_keys_against_independent_definition, ()),
+        (pins.test_tree_oracle_matches_dense_masked_attention, (0,)),
+        (pins.test_tree_oracle_matches_dense_masked_attention, (1,)),
+        (pins.test_one_level_tree_is_the_single_group_oracle, ()),
+        (pins.test_tree_attended_keys_against_independent_definition, ()),
     ]
     return calls
 
 
-def _failing_pins(monkeypatch, rep, smp, grp):
+def _failing_pins(monkeypatch, rep, smp, grp, tre):
     monkeypatch.setattr(pins, "oracle_fwd_bwd", rep.oracle_fwd_bwd)
     monkeypatch.setattr(pins, "rows_fwd_bwd", smp.rows_fwd_bwd)
     monkeypatch.setattr(pins, "keys_dkdv", smp.keys_dkdv)
@@ -75,6 +80,9 @@ def _failing_pins(monkeypatch, rep, smp, grp):
     monkeypatch.setattr(pins, "oracle_groups_fwd_bwd", grp.oracle_groups_fwd_bwd)
     monkeypatch.setattr(pins, "attended_keys_groups", grp.attended_keys_groups)
     monkeypatch.setattr(pins, "group_starts", grp.group_starts)
+    monkeypatch.setattr(pins, "oracle_tree_fwd_bwd", tre.oracle_tree_fwd_bwd)
+    monkeypatch.setattr(pins, "attended_keys_tree", tre.attended_keys_tree)
+    monkeypatch.setattr(pins, "segment_starts", tre.segment_starts)
     failed = []
     with np.errstate(all="ignore"):
         for fn, args in _pin_calls():
@@ -121,6 +129,11 @@ MUTANTS = {
     "groups_keys_not_shifted": (GROUPS, "return s[b] + attended_keys(t - s[b]", "return attended_keys(t - s[b]", 1),
     "groups_dK_from_dV": (GROUPS, 'out["dK"][a:e] = r["dK"]', 'out["dK"][a:e] = r["dV"]', 1),
     "groups_lse_shifted": (GROUPS, 'out["LSE"][:, a:e] = r["LSE"]', 'out["LSE"][:, a:e] = np.roll(r["LSE"], 1, axis=1)', 1),
+    # multi-level prefix trees
+    "tree_dO_not_split": (TREE, "1.0 / n_paths[x]", "1.0", 1),
+    "tree_paths_without_root": (TREE, "paths.append(path[::-1])", "paths.append(path[::-1][1:] or path)", 1),
+    "tree_keys_without_ancestors": (TREE, "parts = [np.arange(s[a], s[a + 1]) for a in anc[::-1]] + [np.arange(s[v], t + 1)]", "parts = [np.arange(s[v], t + 1)]", 1),
+    "tree_dK_not_accumulated": (TREE, "np.add.at(dK[:, g], idx, dkn)", "dK[idx, g] = dkn", 1),
 }
 
 
@@ -130,7 +143,9 @@ def _load_all(path=None, old=None, new=None, nth=1):
     inj = {"oracle_fwd_bwd": rep.oracle_fwd_bwd, "attended_keys": smp.attended_keys}
     grp = (_load(GROUPS, old, new, nth, inject=inj) if path == GROUPS
            else _load(GROUPS, inject=inj))
-    return rep, smp, grp
+    tinj = {"causal_attention_fwd": rep.causal_attention_fwd, "causal_attention_bwd": rep.causal_attention_bwd}
+    tre = (_load(TREE, old, new, nth, inject=tinj) if path == TREE else _load(TREE, inject=tinj))
+    return rep, smp, grp, tre
 
 
 def test_unedited_copy_passes_every_pin(monkeypatch):

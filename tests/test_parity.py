@@ -23,7 +23,8 @@ import torch
 
 from exact_shared_prefix_amd import binding
 from exact_shared_prefix_amd.inputs import WORKLOADS, make_inputs, workload_inputs
-from oracle import group_starts, keys_dkdv, oracle_fwd_bwd, oracle_groups_fwd_bwd, rows_fwd_bwd
+from oracle import (group_starts, keys_dkdv, oracle_fwd_bwd, oracle_groups_fwd_bwd, oracle_tree_fwd_bwd,
+                    rows_fwd_bwd)
 
 pytestmark = pytest.mark.gpu
 
@@ -228,6 +229,56 @@ def test_one_group_call_is_the_single_group_call():
     inp = make_inputs(P, L, 4, 2, 128, seed=43)
     a = run_gpu(inp, deterministic=True)
     b = run_gpu_groups(inp, [(P, L)], deterministic=True)
+    for key in ("O", "LSE", "dQ", "dK", "dV"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+# ------------------------------------------------- multi-level prefix trees --
+TREES = {
+    # depth-first (node_len, node_parent)
+    "system_prompt_two_levels": dict(node_len=[200, 150, 64, 0, 97, 90, 33, 128], node_parent=[-1, 0, 1, 1, 1, 0, 5, 5],
+                                     Hq=4, Hkv=2, d=128, seed=51),
+    "four_levels_d64": dict(node_len=[70, 65, 40, 31, 5, 129], node_parent=[-1, 0, 1, 2, 2, 0],
+                            Hq=4, Hkv=1, d=64, seed=52),
+    "forest_of_trees": dict(node_len=[64, 32, 16, 100, 7, 300, 1], node_parent=[-1, 0, 1, -1, 3, 3, -1],
+                            Hq=8, Hkv=2, d=128, seed=53),
+}
+
+
+def run_gpu_tree(inp, node_len, node_parent, deterministic=False):
+    dev = torch.device("cuda:0")
+    q, k, v, do = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.do))
+    tp = binding.TreePacking(node_len, node_parent)
+    o, lse = binding.fwd_tree(q, k, v, tp, inp.scale)
+    dq, dk, dv = binding.bwd_tree(q, k, v, o, lse, do, tp, inp.scale, deterministic=deterministic)
+    torch.cuda.synchronize()
+    return {kk: t.float().cpu().numpy() for kk, t in
+            {"O": o, "LSE": lse, "dQ": dq, "dK": dk, "dV": dv}.items()}
+
+
+@pytest.mark.parametrize("name", sorted(TREES))
+def test_tree_elementwise(name):
+    c = TREES[name]
+    T = sum(c["node_len"])
+    inp = make_inputs(0, [T], c["Hq"], c["Hkv"], c["d"], seed=c["seed"])
+    say(f"case tree {name}: {c['node_len']} {c['node_parent']}")
+    got = run_gpu_tree(inp, c["node_len"], c["node_parent"])
+    ref = oracle_tree_fwd_bwd(np64(inp.q), np64(inp.k), np64(inp.v), np64(inp.do), c["node_len"],
+                              c["node_parent"], inp.scale)
+    for key in ("O", "dQ", "dK", "dV"):
+        e = rel(got[key], ref[key])
+        say(f"  {key}: rel {e:.2e}")
+        assert e <= REL, key
+    assert float(np.max(np.abs(got["LSE"] - ref["LSE"]))) <= LSE_ABS
+    for key, x in got.items():
+        assert np.all(np.isfinite(x)), key
+
+
+def test_one_level_tree_call_is_the_single_group_call():
+    P, L = 300, [129, 1, 0, 64, 250]
+    inp = make_inputs(P, L, 4, 2, 128, seed=54)
+    a = run_gpu(inp, deterministic=True)
+    b = run_gpu_tree(inp, [P] + L, [-1] + [0] * len(L), deterministic=True)
     for key in ("O", "LSE", "dQ", "dK", "dV"):
         assert np.array_equal(a[key], b[key]), key
 
