@@ -430,6 +430,71 @@ def layer_main(args) -> int:
     return 0
 
 
+def tree_main(args) -> int:
+    """Two-level shared prefix: a system prompt of S tokens shared by B prompt
+    groups (P tokens each, N responses of R), fwd+bwd through the tree entry
+    points (the system prompt stored once), against the same batch as B flat
+    groups (each group carrying its own copy of the system prompt) and against
+    the fully replicated layout (every sequence carries both prefixes)."""
+    import torch
+
+    from exact_shared_prefix_amd import binding
+    from exact_shared_prefix_amd.inputs import make_inputs
+
+    S, B, P, N, R = 4096, 4, 2048, 8, 1024
+    Hq, Hkv, d = 32, 8, 128
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    steps, warmup = max(3, args.steps // 2), 2
+    node_len, node_parent = [S], [-1]
+    for _ in range(B):
+        node_parent.append(0)
+        node_len.append(P)
+        g = len(node_len) - 1
+        node_len += [R] * N
+        node_parent += [g] * N
+
+    def timed(T, fwd, bwd):
+        inp = make_inputs(0, [T], Hq, Hkv, d, seed=10)
+        q, k, v, do = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.do))
+        torch.cuda.reset_peak_memory_stats(dev)
+        s = torch.cuda.current_stream()
+        for _ in range(warmup):
+            o, lse = fwd(q, k, v)
+            bwd(q, k, v, o, lse, do)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(steps):
+            o, lse = fwd(q, k, v)
+            bwd(q, k, v, o, lse, do)
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps, torch.cuda.max_memory_allocated(dev)
+
+    tp = binding.TreePacking(node_len, node_parent)
+    log(f"[tree] system prompt {S} + {B} x (prompt {P} + {N} x {R}): T={tp.T}")
+    ms_t, mem_t = timed(tp.T, lambda q, k, v: binding.fwd_tree(q, k, v, tp),
+                        lambda q, k, v, o, lse, do: binding.bwd_tree(q, k, v, o, lse, do, tp))
+    gp = binding.GroupPacking([(S + P, [R] * N)] * B)
+    ms_g, mem_g = timed(gp.T, lambda q, k, v: binding.fwd_groups(q, k, v, gp),
+                        lambda q, k, v, o, lse, do: binding.bwd_groups(q, k, v, o, lse, do, gp))
+    rp = binding.Packing(0, [S + P + R] * (B * N))
+    ms_r, mem_r = timed(rp.T, lambda q, k, v: binding.fwd(q, k, v, rp),
+                        lambda q, k, v, o, lse, do: binding.bwd(q, k, v, o, lse, do, rp))
+    rec = {"metric": "two-level shared prefix: fwd+bwd ms, tree vs flat groups vs replicated",
+           "config": {"system_prompt": S, "groups": B, "P": P, "N": N, "R": R, "Hq": Hq, "Hkv": Hkv,
+                      "head_dim": d},
+           "tree": {"tokens": tp.T, "ms": ms_t, "peak_hbm_gb": mem_t / 1e9},
+           "flat_groups": {"tokens": gp.T, "ms": ms_g, "peak_hbm_gb": mem_g / 1e9},
+           "replicated": {"tokens": rp.T, "ms": ms_r, "peak_hbm_gb": mem_r / 1e9},
+           "speedup_tree_over_groups": ms_g / ms_t, "speedup_tree_over_replicated": ms_r / ms_t,
+           "steps": steps}
+    log(f"[tree] tree {ms_t:.2f} ms, flat groups {ms_g:.2f} ms, replicated {ms_r:.2f} ms")
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -442,6 +507,8 @@ def main() -> int:
     ap.add_argument("--no-mfma-peak", action="store_true", help="skip the measured MFMA peak")
     ap.add_argument("--layer", action="store_true",
                     help="one packed decoder layer (random weights) vs the replicated layout")
+    ap.add_argument("--tree", action="store_true",
+                    help="two-level shared prefix (system prompt + prompt groups) vs flat groups")
     ap.add_argument("--sweep", action="store_true",
                     help="N/P/R sweep of packed vs replicated time (one JSON line per point)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -469,6 +536,8 @@ def main() -> int:
         return sweep_main(args)
     if args.layer:
         return layer_main(args)
+    if args.tree:
+        return tree_main(args)
     name = args.workload or HEADLINE
     if name in GROUP_WORKLOADS:
         return group_main(args, name)
