@@ -69,8 +69,11 @@ __global__ __launch_bounds__(256) void zero_kernel(float4* __restrict__ p, size_
 //   dV += P^T dO, dK += dS^T Q.
 // S and dP are computed with queries as rows, so a lane owns one key and the
 // P / dS accumulators are directly the A operands of the dV / dK products.
-// Q and dO arrive as A-operand fragments by direct copies one step ahead; the
-// Q^T, dO^T B fragments are made per step, one d tile per wave.
+// Q and dO arrive by direct copies one step ahead. For d = 128 they are
+// swizzled row tiles, read as A fragments by 16-byte reads and as the B
+// fragments of the dV, dK products by transposing reads; for d = 64 they are
+// A-operand fragments and the Q^T, dO^T B fragments are made per step by MFMA
+// transposes, one d tile per wave.
 template <int D>
 __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
@@ -83,6 +86,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
   constexpr int NDT = D / 32;     // 32-wide d tiles
   static_assert(kBwdKeys == 32 * NW, "one 32-key block per wave");
   static_assert((2 * NKK) % NW == 0 && 2 * NDT <= NW, "copies and transposes per wave");
+  constexpr bool kRow = D == 128;   // row tiles and transposing reads
   __shared__ __attribute__((aligned(16))) u16 QA0[NKK * kFrag];
   __shared__ __attribute__((aligned(16))) u16 QA1[NKK * kFrag];
   __shared__ __attribute__((aligned(16))) u16 OA0[NKK * kFrag];
@@ -90,8 +94,9 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
   __shared__ __attribute__((aligned(16))) float LD0[NW * 64];   // per wave: LSE (32) | D (32)
   __shared__ __attribute__((aligned(16))) float LD1[NW * 64];
   __shared__ __attribute__((aligned(16))) u16 KF[NW * NKK * kFrag];   // K B fragments per wave
-  __shared__ __attribute__((aligned(16))) u16 QT[NDT * 2 * kFrag];    // Q^T B fragments [dt][ks]
-  __shared__ __attribute__((aligned(16))) u16 OT[NDT * 2 * kFrag];    // dO^T B fragments
+  // Q^T, dO^T B fragments [dt][ks] (d = 64 only)
+  __shared__ __attribute__((aligned(16))) u16 QT[kRow ? 8 : NDT * 2 * kFrag];
+  __shared__ __attribute__((aligned(16))) u16 OT[kRow ? 8 : NDT * 2 * kFrag];
 
   int item_id, g;
   if (!headmap_decode(hm, blockIdx.x, item_id, g)) return;
@@ -136,16 +141,30 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
   auto stage = [&](int st, u16* qa, u16* oa, float* ld) {
     const int qb = it.r0 + (st / G) * BQ, h = g * G + st % G;
     const int row = min(qb + l32, it.r1 - 1);
-    const u16* qp = q + (size_t)row * qrow + (size_t)h * D + 8 * hl;
-    const u16* op = dO + (size_t)row * qrow + (size_t)h * D + 8 * hl;
+    if constexpr (kRow) {
+      // 1 KB copy f of [Q | dO]: rows 4 m .. 4 m + 3 of the row tile, m = f % NKK
 #pragma unroll
-    for (int j = 0; j < 2 * NKK / NW; ++j) {
-      const int f = w + NW * j;
-      if (f < NKK) dma16(qp + 16 * f, qa + f * kFrag);
-      else dma16(op + 16 * (f - NKK), oa + (f - NKK) * kFrag);
+      for (int j = 0; j < 2 * NKK / NW; ++j) {
+        const int f = w + NW * j, m = f % NKK;
+        const int r = 4 * m + (lane >> 4);
+        const int chunk = (lane & 15) ^ row_swz(r);
+        const size_t src = (size_t)min(qb + r, it.r1 - 1) * qrow + (size_t)h * D + 8 * chunk;
+        if (f < NKK) dma16(q + src, qa + m * kFrag);
+        else dma16(dO + src, oa + m * kFrag);
+      }
+    } else {
+      const u16* qp = q + (size_t)row * qrow + (size_t)h * D + 8 * hl;
+      const u16* op = dO + (size_t)row * qrow + (size_t)h * D + 8 * hl;
+#pragma unroll
+      for (int j = 0; j < 2 * NKK / NW; ++j) {
+        const int f = w + NW * j;
+        if (f < NKK) dma16(qp + 16 * f, qa + f * kFrag);
+        else dma16(op + 16 * (f - NKK), oa + (f - NKK) * kFrag);
+      }
     }
     dma4((hl ? delta : lse) + (size_t)h * T + row, ld + 64 * w);
   };
+  const uint32_t abase = row_a_base(lane), bbase = row_b_base(lane);
 
   auto step = [&](int st, const u16* qa, const u16* oa, const float* ld, u16* qan, u16* oan,
                   float* ldn) {
@@ -153,7 +172,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
     vm_barrier<0>();   // this step's copies landed; every wave is done with the last step
 
     // Q^T (job < NDT) and dO^T B fragments of d tile job % NDT
-    if (w < 2 * NDT) {
+    if (!kRow && w < 2 * NDT) {
       const int dt = w % NDT;
       const u16* src = w < NDT ? qa : oa;
       u16* dst = w < NDT ? QT : OT;
@@ -171,7 +190,8 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
       f32x16 sacc = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk)
-        sacc = mfma32(frag_ld(qa + kk * kFrag, lane), frag_ld(kfl + kk * kFrag, lane), sacc);
+        sacc = mfma32(kRow ? row_ld_a(qa, abase ^ (32 * kk)) : frag_ld(qa + kk * kFrag, lane),
+                      frag_ld(kfl + kk * kFrag, lane), sacc);
       pipelined_mfma<NKK, 2, 2>();
       const float* lw = ld + 64 * w;
       if ((kw + 31 > qb) || (kw + 32 > it.ke) || (qb + BQ > it.r1)) {
@@ -199,7 +219,8 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
 
       f32x16 dpacc = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) dpacc = mfma32(frag_ld(oa + kk * kFrag, lane), vf[kk], dpacc);
+      for (int kk = 0; kk < NKK; ++kk)
+        dpacc = mfma32(kRow ? row_ld_a(oa, abase ^ (32 * kk)) : frag_ld(oa + kk * kFrag, lane), vf[kk], dpacc);
       pipelined_mfma<NKK, 1, 4>();
       if (st + 1 < nsteps) stage(st + 1, qan, oan, ldn);
 #pragma unroll
@@ -216,6 +237,26 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
       pack2(dpacc, sf[0], sf[1]);
     }
     if (!active && st + 1 < nsteps) stage(st + 1, qan, oan, ldn);
+
+    if constexpr (kRow) {
+      if (active) {
+        // dV[key][d] += P^T dO, dK[key][d] += dS^T Q, B fragments by transposing reads
+        auto bfrag = [&](const u16* tile, int dt, int ks) __attribute__((always_inline)) {
+          return row_ld_b(tile, 4096 * ks + (bbase ^ (64 * dt)), 4096 * ks + 2048 + (bbase ^ (64 * dt + 32)));
+        };
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) dvacc[dt] = mfma32(pf[ks], bfrag(oa, dt, ks), dvacc[dt]);
+        pipelined_mfma<2 * NDT, 2, 2>();
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) dkacc[dt] = mfma32(sf[ks], bfrag(qa, dt, ks), dkacc[dt]);
+        pipelined_mfma<2 * NDT, 2, 2>();
+      }
+      return;
+    }
     lds_barrier();   // Q^T, dO^T fragments complete
 
     if (active) {

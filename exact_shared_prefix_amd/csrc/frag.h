@@ -87,6 +87,44 @@ __device__ __forceinline__ float bf16_elem(const bf16x8& f, int e) {
   return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
 }
 
+// Row-major 32 x 128 bf16 tiles with an XOR swizzle ("row tiles"). Row r is
+// 256 bytes; its 16-byte chunk c sits at chunk position c ^ row_swz(r). The
+// swizzle makes both ways a tile is read free of LDS bank conflicts: A
+// fragments (lane -> row l % 32, 8 consecutive columns) by 16-byte reads, and
+// B fragments with k running over rows (lane -> column, 8 rows) by the
+// transposing 8-byte read, which gives lane i of each 16-lane group, in slot j,
+// element i % 4 of the 4 elements addressed by lane i / 4 + 4 j of its group.
+// A tile is copied by 8 direct copies of 1 KB (4 rows each), lane l of copy m
+// fetching row 4 m + l / 16, chunk (l % 16) ^ row_swz(4 m + l / 16).
+__device__ __forceinline__ int row_swz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+
+// Byte offsets of this lane's reads: A fragment kk of a tile is at
+// row_a_base(lane) ^ (32 kk); the B fragment (d tile dt, 16-row step ks) is
+// the pair of transposing reads at 4096 ks + 2048 h + (row_b_base(lane) ^
+// (64 dt + 32 h)), h = 0, 1, holding rows 16 ks + 8 h + 4 (lane / 32) + 0..3.
+__device__ __forceinline__ uint32_t row_a_base(int lane) {
+  const int r = lane & 31, hl = lane >> 5;
+  return 256 * r + 16 * (row_swz(r) ^ hl);
+}
+__device__ __forceinline__ uint32_t row_b_base(int lane) {
+  const int g = lane >> 4, L = lane & 15, a = L & 3, j = L >> 2, hl = g >> 1, x = g & 1;
+  return 1024 * hl + 320 * j + 8 * (a & 1) + 16 * ((2 * x + (a >> 1)) ^ hl);
+}
+__device__ __forceinline__ bf16x8 row_ld_a(const u16* tile, uint32_t off) {
+  return lds_b128(reinterpret_cast<const u16*>(reinterpret_cast<const char*>(tile) + off));
+}
+typedef short tr4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8 row_ld_b(const u16* tile, uint32_t off0, uint32_t off1) {
+  typedef __attribute__((address_space(3))) tr4_t lds_tr4;
+  char* t = const_cast<char*>(reinterpret_cast<const char*>(tile));
+  const tr4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr4*)(t + off0));
+  const tr4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr4*)(t + off1));
+  Frag f;
+  f.h[0] = __builtin_bit_cast(uint2, x0);
+  f.h[1] = __builtin_bit_cast(uint2, x1);
+  return f.v;
+}
+
 // Wait until at most N vector-memory operations of this wave (the direct
 // copies above included) are outstanding, then an LDS barrier.
 template <int N>
