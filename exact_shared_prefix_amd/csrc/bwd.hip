@@ -356,8 +356,11 @@ __global__ __launch_bounds__(256) void reduce_kernel(
 // forward: for each 64-key tile, S^T = K Q^T, P^T = exp2(S^T c - LSE log2 e),
 // dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T. dQ stays in
 // registers and is written once, so no atomics are needed. K and V tiles
-// arrive by direct global -> LDS copies one tile ahead as A-operand fragments;
-// K^T fragments are made from them by MFMA transposes.
+// arrive by direct global -> LDS copies one tile ahead, V as A-operand
+// fragments. For d = 128 each 32-key block of K is a swizzled row tile, read as
+// the A fragments of S^T and, by transposing reads, as the K^T A fragments of
+// the dQ product; for d = 64, K arrives as A fragments and K^T is made from
+// them by MFMA transposes.
 
 template <int D>
 __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
@@ -372,11 +375,12 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
   constexpr int NTF = 2 * NKK;    // K (or V) fragments per tile: 2 key blocks x NKK
   constexpr int NJOB = 2 * NTF;   // copies per tile (K and V)
   static_assert(NJOB % NW == 0, "copies per wave");
+  constexpr bool kRow = D == 128;   // K as row tiles, K^T by transposing reads
   __shared__ __attribute__((aligned(16))) u16 KA0[NTF * kFrag];
   __shared__ __attribute__((aligned(16))) u16 KA1[NTF * kFrag];
   __shared__ __attribute__((aligned(16))) u16 VA0[NTF * kFrag];
   __shared__ __attribute__((aligned(16))) u16 VA1[NTF * kFrag];
-  __shared__ __attribute__((aligned(16))) u16 KT[2 * NDT * 2 * kFrag];   // [kb2][dt][ks]
+  __shared__ __attribute__((aligned(16))) u16 KT[kRow ? 8 : 2 * NDT * 2 * kFrag];   // [kb2][dt][ks], d = 64
 
   int item_id, h;
   if (!headmap_decode(hm, blockIdx.x, item_id, h)) return;
@@ -386,6 +390,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept in a scalar register
   const int hl = lane >> 5, l32 = lane & 31;
+  const uint32_t abase = row_a_base(lane), bbase = row_b_base(lane);
   const int t0 = it.r0 + 32 * w;   // first query row of this wave
   const int t = t0 + l32;          // this lane's query row
   const int tc = min(t, it.r1 - 1);
@@ -455,9 +460,17 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
     for (int j = 0; j < NJOB / NW; ++j) {
       const int f = w + NW * j;
       const int kb2 = (f / NKK) % 2, kk = f % NKK;
-      const int key = min(kb + 32 * kb2 + l32, ke - 1);
-      const u16* src = (f < NTF ? k : v) + (size_t)key * krow + (size_t)g * D + 16 * kk + 8 * hl;
-      dma16(src, (f < NTF ? ka : va) + (f % NTF) * kFrag);
+      if (kRow && f < NTF) {
+        // rows 4 kk .. 4 kk + 3 of K row tile kb2
+        const int r = 4 * kk + (lane >> 4);
+        const int key = min(kb + 32 * kb2 + r, ke - 1);
+        const int chunk = (lane & 15) ^ row_swz(r);
+        dma16(k + (size_t)key * krow + (size_t)g * D + 8 * chunk, ka + f * kFrag);
+      } else {
+        const int key = min(kb + 32 * kb2 + l32, ke - 1);
+        const u16* src = (f < NTF ? k : v) + (size_t)key * krow + (size_t)g * D + 16 * kk + 8 * hl;
+        dma16(src, (f < NTF ? ka : va) + (f % NTF) * kFrag);
+      }
     }
   };
 
@@ -468,7 +481,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
     if (i + 1 < ntiles) stage(i + 1, kan, van);
     // K^T A fragments (lane -> d, k-slots in accumulator key order)
 #pragma unroll
-    for (int p = w; p < 2 * NDT; p += NW) {
+    for (int p = w; !kRow && p < 2 * NDT; p += NW) {
       const int kb2 = p / NDT, dt = p % NDT;
       bf16x8 f0, f1;
       pack2(xpose_nat(frag_ld(ka + (kb2 * NKK + 2 * dt) * kFrag, lane),
@@ -477,7 +490,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
       frag_st(KT + ((kb2 * NDT + dt) * 2) * kFrag, lane, f0);
       frag_st(KT + ((kb2 * NDT + dt) * 2 + 1) * kFrag, lane, f1);
     }
-    lds_barrier();
+    if (!kRow) lds_barrier();
     if (!wave_rows) return;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -486,7 +499,10 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
       // S^T[key][query]: register r <-> key k0 + 8 (r/4) + 4 hl + r%4
       f32x16 sacc = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) sacc = mfma32(frag_ld(ka + (kb2 * NKK + kk) * kFrag, lane), qf[kk], sacc);
+      for (int kk = 0; kk < NKK; ++kk)
+        sacc = mfma32(kRow ? row_ld_a(ka + kb2 * NKK * kFrag, abase ^ (32 * kk))
+                           : frag_ld(ka + (kb2 * NKK + kk) * kFrag, lane),
+                      qf[kk], sacc);
       pipelined_mfma<NKK, 1, 4>();
       const bool need_mask = (k0 + 31 > t0) || (k0 + 32 > ke);
       if (need_mask) {
@@ -510,12 +526,23 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
       for (int r = 0; r < 16; ++r) dpacc[r] = bf16_elem(pf[r >> 3], r & 7) * (dpacc[r] - dl);
       bf16x8 sf[2];
       pack2(dpacc, sf[0], sf[1]);
+      if constexpr (kRow) {
+        const u16* kt = ka + kb2 * NKK * kFrag;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
+        for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          dqacc[dt] = mfma32(frag_ld(KT + ((kb2 * NDT + dt) * 2 + ks) * kFrag, lane), sf[ks], dqacc[dt]);
-      pipelined_mfma<2 * NDT, 1, 4>();
+          for (int ks = 0; ks < 2; ++ks)
+            dqacc[dt] = mfma32(row_ld_b(kt, 4096 * ks + (bbase ^ (64 * dt)), 4096 * ks + 2048 + (bbase ^ (64 * dt + 32))),
+                               sf[ks], dqacc[dt]);
+        pipelined_mfma<2 * NDT, 2, 2>();
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+            dqacc[dt] = mfma32(frag_ld(KT + ((kb2 * NDT + dt) * 2 + ks) * kFrag, lane), sf[ks], dqacc[dt]);
+        pipelined_mfma<2 * NDT, 1, 4>();
+      }
     }
   };
 
