@@ -23,7 +23,7 @@ hipError_t launch_xpose_kv(const Problem& pb, const void* src, void* dst, const 
 hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dO, void* dQ, void* dK,
                       void* dV, const BwdItem* items_dev, int n_items, const FwdItem* qitems_dev,
-                      const Region* qregions_dev, int n_qitems, float* delta, float* dk_acc,
+                      const Region* qregions_dev, int n_qitems, float2* rs, float* dk_acc,
                       float* dv_acc, float* part,
                       const int* tile_off, const int* tile_items, int n_tiles, hipStream_t stream,
                       int phase_mask);
@@ -329,7 +329,7 @@ BwdLayout bwd_layout(const Problem& pb, size_t n_items, size_t n_qitems, size_t 
   L.items = off;    off = align_up(off + n_items * sizeof(BwdItem));
   L.qitems = off;   off = align_up(off + n_qitems * sizeof(FwdItem));
   L.qregions = off; off = align_up(off + std::max<size_t>(1, n_qregions) * sizeof(Region));
-  L.delta = off;  off = align_up(off + (size_t)pb.Hq * pb.T * sizeof(float));
+  L.delta = off;  off = align_up(off + (size_t)pb.Hq * pb.T * 2 * sizeof(float));   // {-LSE log2 e, D}
   if (det) {
     L.part = off;       off = align_up(off + n_items * pb.Hkv * 2 * (size_t)kBwdKeys * pb.d * sizeof(float));
     L.tile_off = off;   off = align_up(off + (n_tiles + 1) * sizeof(int));
@@ -428,7 +428,7 @@ dualkv_status bwd_impl(Problem& pb, const void* q, const void* k, const void* v,
   if (launch_bwd(pb, q, k, v, o, lse, dO, dQ, dK, dV, reinterpret_cast<const BwdItem*>(ws + L.items),
                  (int)items.size(), reinterpret_cast<const FwdItem*>(ws + L.qitems),
                  reinterpret_cast<const Region*>(ws + L.qregions), (int)qitems.size(),
-                 reinterpret_cast<float*>(ws + L.delta),
+                 reinterpret_cast<float2*>(ws + L.delta),
                  det ? nullptr : reinterpret_cast<float*>(ws + L.dk),
                  det ? nullptr : reinterpret_cast<float*>(ws + L.dv),
                  det ? reinterpret_cast<float*>(ws + L.part) : nullptr,

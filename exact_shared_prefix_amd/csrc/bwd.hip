@@ -28,10 +28,13 @@ namespace dkv {
 
 // ------------------------------------------------------------------ pre --
 // One 16-lane group per (row, head): 16 lanes x 8 elements = 128 (d=64: 8 lanes).
+// Writes rs[h][t] = {-LSE_t log2 e, D_t}: the two per-row values both passes
+// read, the LSE already in the base-2 form the exponentials use.
 template <int D>
 __global__ __launch_bounds__(256) void pre_kernel(const u16* __restrict__ o,
                                                   const u16* __restrict__ dO,
-                                                  float* __restrict__ delta, int T, int Hq) {
+                                                  const float* __restrict__ lse,
+                                                  float2* __restrict__ rs, int T, int Hq) {
   constexpr int LPR = D / 8;  // lanes per (row, head)
   const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long rh = gid / LPR;   // row * Hq + head
@@ -52,7 +55,8 @@ __global__ __launch_bounds__(256) void pre_kernel(const u16* __restrict__ o,
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (valid && sub == 0) {
     const int t = (int)(rh / Hq), h = (int)(rh % Hq);
-    delta[(size_t)h * T + t] = acc;
+    const size_t i = (size_t)h * T + t;
+    rs[i] = make_float2(-lse[i] * kLog2e, acc);
   }
 }
 
@@ -62,6 +66,50 @@ __global__ __launch_bounds__(256) void zero_kernel(float4* __restrict__ p, size_
 }
 
 // -------------------------------------------------------------------- dKV --
+// End of a dK/dV work item: wave w's 32 keys of dK, dV (accumulator layout:
+// lane -> d column 32 dt + l % 32, register r -> key 8 (r/4) + 4 (l/32) + r%4).
+// Atomic mode adds them to the fp32 accumulators (where the N sequences'
+// prompt gradients meet; keys past the tile end add exact zeros to the tile's
+// last key). Deterministic mode stores the item's partials
+// ([item][g][key][d], dK then dV), summed in item order by reduce_kernel.
+template <int D>
+__device__ __forceinline__ void store_dkv(const f32x16* dkacc, const f32x16* dvacc,
+                                          float* __restrict__ dk_acc, float* __restrict__ dv_acc,
+                                          float* __restrict__ part, const BwdItem& it, int item_id,
+                                          int g, int w, int lane, int Hkv) {
+  constexpr int NDT = D / 32;
+  const int hl = lane >> 5, l32 = lane & 31;
+  if (part) {
+    float* pk = part + ((size_t)item_id * Hkv + g) * (size_t)(2 * kBwdKeys * D) + 32 * w * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kl = 8 * (r >> 2) + 4 * hl + (r & 3);
+        pk[kl * D + 32 * dt + l32] = dkacc[dt][r];
+        pk[(size_t)kBwdKeys * D + kl * D + 32 * dt + l32] = dvacc[dt][r];
+      }
+    return;
+  }
+  const int kw = it.kb + 32 * w;
+  const size_t krow = (size_t)Hkv * D;
+  if (kw < it.ke) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      float* dkp = dk_acc + (size_t)g * D + 32 * dt + l32;
+      float* dvp = dv_acc + (size_t)g * D + 32 * dt + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kk = kw + 8 * (r >> 2) + 4 * hl + (r & 3);
+        const size_t off = (size_t)min(kk, it.ke - 1) * krow;
+        const bool ok = kk < it.ke;
+        unsafeAtomicAdd(dkp + off, ok ? dkacc[dt][r] : 0.f);
+        unsafeAtomicAdd(dvp + off, ok ? dvacc[dt][r] : 0.f);
+      }
+    }
+  }
+}
+
 // Wave w owns keys kb + 32 w .. + 31: V fragments and the dK, dV accumulators
 // in registers, K fragments in its own LDS slots. Per 32-row step (query rows
 // qb.., head h):
@@ -77,7 +125,7 @@ __global__ __launch_bounds__(256) void zero_kernel(float4* __restrict__ p, size_
 template <int D>
 __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
-    const u16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
+    const u16* __restrict__ dO, const float2* __restrict__ rs,
     float* __restrict__ dk_acc, float* __restrict__ dv_acc, float* __restrict__ part,
     const BwdItem* __restrict__ items, HeadMap hm, int T, int Hq, int Hkv, float c) {
   constexpr int NW = kBwdWaves;
@@ -87,16 +135,21 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
   static_assert(kBwdKeys == 32 * NW, "one 32-key block per wave");
   static_assert((2 * NKK) % NW == 0 && 2 * NDT <= NW, "copies and transposes per wave");
   constexpr bool kRow = D == 128;   // row tiles and transposing reads
-  __shared__ __attribute__((aligned(16))) u16 QA0[NKK * kFrag];
-  __shared__ __attribute__((aligned(16))) u16 QA1[NKK * kFrag];
-  __shared__ __attribute__((aligned(16))) u16 OA0[NKK * kFrag];
-  __shared__ __attribute__((aligned(16))) u16 OA1[NKK * kFrag];
-  __shared__ __attribute__((aligned(16))) float LD0[NW * 64];   // per wave: LSE (32) | D (32)
-  __shared__ __attribute__((aligned(16))) float LD1[NW * 64];
-  __shared__ __attribute__((aligned(16))) u16 KF[NW * NKK * kFrag];   // K B fragments per wave
+  // One LDS block with the step buffers first: every read of a Q / dO tile is
+  // then a per-lane base register plus an immediate offset below 64 KB.
+  constexpr int TS = NKK * kFrag;             // u16 per Q or dO tile
+  constexpr int XS = kRow ? 8 : NDT * 2 * kFrag;
+  __shared__ __attribute__((aligned(16))) u16 smem[4 * TS + 2 * NW * 64 * 2 + NW * TS + 2 * XS];
+  u16* const QA0 = smem;
+  u16* const QA1 = smem + TS;
+  u16* const OA0 = smem + 2 * TS;
+  u16* const OA1 = smem + 3 * TS;
+  float* const LD0 = reinterpret_cast<float*>(smem + 4 * TS);   // per wave: -LSE log2 e (32) | D (32)
+  float* const LD1 = LD0 + NW * 64;
+  u16* const KF = reinterpret_cast<u16*>(LD1 + NW * 64);          // K B fragments per wave
   // Q^T, dO^T B fragments [dt][ks] (d = 64 only)
-  __shared__ __attribute__((aligned(16))) u16 QT[kRow ? 8 : NDT * 2 * kFrag];
-  __shared__ __attribute__((aligned(16))) u16 OT[kRow ? 8 : NDT * 2 * kFrag];
+  u16* const QT = KF + NW * TS;
+  u16* const OT = QT + XS;
 
   int item_id, g;
   if (!headmap_decode(hm, blockIdx.x, item_id, g)) return;
@@ -138,19 +191,21 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
   // Copies for step st: fragments f = w, w + NW, ... of [Q | dO], and this
   // wave's own copy of the 32 LSE and D values. Rows past the chunk end read
   // its last row; their P is masked to zero.
-  auto stage = [&](int st, u16* qa, u16* oa, float* ld) {
-    const int qb = it.r0 + (st / G) * BQ, h = g * G + st % G;
+  auto stage = [&](int qb, int h, u16* qa, u16* oa, float* ld) {
     const int row = min(qb + l32, it.r1 - 1);
+    const int lim = it.r1 - 1 - qb;   // last valid row of the step, relative to qb
     if constexpr (kRow) {
-      // 1 KB copy f of [Q | dO]: rows 4 m .. 4 m + 3 of the row tile, m = f % NKK
+      // 1 KB copy f of [Q | dO]: rows 4 m .. 4 m + 3 of the row tile, m = f % NKK;
+      // wave-uniform base (row qb, head h) plus a 32-bit per-lane byte offset
+      const size_t base = (size_t)qb * qrow + (size_t)h * D;
 #pragma unroll
       for (int j = 0; j < 2 * NKK / NW; ++j) {
         const int f = w + NW * j, m = f % NKK;
         const int r = 4 * m + (lane >> 4);
-        const int chunk = (lane & 15) ^ row_swz(r);
-        const size_t src = (size_t)min(qb + r, it.r1 - 1) * qrow + (size_t)h * D + 8 * chunk;
-        if (f < NKK) dma16(q + src, qa + m * kFrag);
-        else dma16(dO + src, oa + m * kFrag);
+        const uint32_t chunk = (uint32_t)((lane & 15) ^ row_swz(r));
+        const uint32_t voff = 2u * ((uint32_t)min(r, lim) * (uint32_t)qrow + 8u * chunk);
+        if (f < NKK) dma16s(q + base, voff, qa + m * kFrag);
+        else dma16s(dO + base, voff, oa + m * kFrag);
       }
     } else {
       const u16* qp = q + (size_t)row * qrow + (size_t)h * D + 8 * hl;
@@ -162,13 +217,15 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
         else dma16(op + 16 * (f - NKK), oa + (f - NKK) * kFrag);
       }
     }
-    dma4((hl ? delta : lse) + (size_t)h * T + row, ld + 64 * w);
+    // lane l < 32: -LSE log2 e of row qb + l; lane 32 + l: D of that row
+    dma4s(rs + (size_t)h * T + qb, 4u * (2u * (uint32_t)min(l32, lim) + (uint32_t)hl), ld + 64 * w);
   };
   const uint32_t abase = row_a_base(lane), bbase = row_b_base(lane);
 
-  auto step = [&](int st, const u16* qa, const u16* oa, const float* ld, u16* qan, u16* oan,
-                  float* ldn) {
-    const int qb = it.r0 + (st / G) * BQ;
+  // step st covers rows qb .. qb + 31 of query head g G + st % G; (nq, nh) is
+  // the row block and head of step st + 1, whose copies it issues
+  auto step = [&](int st, int qb, int nq, int nh, const u16* qa, const u16* oa, const float* ld,
+                  u16* qan, u16* oan, float* ldn) {
     vm_barrier<0>();   // this step's copies landed; every wave is done with the last step
 
     // Q^T (job < NDT) and dO^T B fragments of d tile job % NDT
@@ -198,11 +255,11 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const float4 l4 = *reinterpret_cast<const float4*>(lw + 8 * g4 + 4 * hl);
-          const float la[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
+          const float la[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int row = qb + 8 * g4 + 4 * hl + e;
-            const float p = fast_exp2(fmaf(sacc[4 * g4 + e], c, -la[e]));
+            const float p = fast_exp2(fmaf(sacc[4 * g4 + e], c, la[e]));
             sacc[4 * g4 + e] = (key > row || key >= it.ke || row >= it.r1) ? 0.f : p;
           }
         }
@@ -210,9 +267,9 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const float4 l4 = *reinterpret_cast<const float4*>(lw + 8 * g4 + 4 * hl);
-          const float la[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
+          const float la[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sacc[4 * g4 + e] = fast_exp2(fmaf(sacc[4 * g4 + e], c, -la[e]));
+          for (int e = 0; e < 4; ++e) sacc[4 * g4 + e] = fast_exp2(fmaf(sacc[4 * g4 + e], c, la[e]));
         }
       }
       pack2(sacc, pf[0], pf[1]);
@@ -222,7 +279,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
       for (int kk = 0; kk < NKK; ++kk)
         dpacc = mfma32(kRow ? row_ld_a(oa, abase ^ (32 * kk)) : frag_ld(oa + kk * kFrag, lane), vf[kk], dpacc);
       pipelined_mfma<NKK, 1, 4>();
-      if (st + 1 < nsteps) stage(st + 1, qan, oan, ldn);
+      if (st + 1 < nsteps) stage(nq, g * G + nh, qan, oan, ldn);
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const float4 d4 = *reinterpret_cast<const float4*>(lw + 32 + 8 * g4 + 4 * hl);
@@ -230,13 +287,12 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g4 + e;
-          // dS from the bf16 P that the dV product uses
-          dpacc[r] = bf16_elem(pf[r >> 3], r & 7) * (dpacc[r] - da[e]);
+          dpacc[r] = sacc[r] * (dpacc[r] - da[e]);   // dS from the fp32 P
         }
       }
       pack2(dpacc, sf[0], sf[1]);
     }
-    if (!active && st + 1 < nsteps) stage(st + 1, qan, oan, ldn);
+    if (!active && st + 1 < nsteps) stage(nq, g * G + nh, qan, oan, ldn);
 
     if constexpr (kRow) {
       if (active) {
@@ -275,43 +331,26 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
   };
 
   // The step loop alternates between two statically distinct buffer sets.
-  if (nsteps > 0) stage(0, QA0, OA0, LD0);
+  // (cq, ch): row block and head offset of the current step, kept in scalar
+  // registers and advanced head first
+  int cq = it.r0, ch = 0;
+  auto advance = [&](int& q_, int& h_) __attribute__((always_inline)) {
+    if (++h_ == G) { h_ = 0; q_ += BQ; }
+  };
+  if (nsteps > 0) stage(cq, g * G, QA0, OA0, LD0);
   for (int st = 0; st < nsteps; st += 2) {
-    step(st, QA0, OA0, LD0, QA1, OA1, LD1);
-    if (st + 1 < nsteps) step(st + 1, QA1, OA1, LD1, QA0, OA0, LD0);
-  }
-
-  if (part) {
-    // deterministic mode: this item's partial dK, dV for all kBwdKeys keys
-    // ([item][g][key][d], dK then dV), summed in item order by reduce_kernel
-    float* pk = part + ((size_t)item_id * Hkv + g) * (size_t)(2 * kBwdKeys * D) + 32 * w * D;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kl = 8 * (r >> 2) + 4 * hl + (r & 3);
-        pk[kl * D + 32 * dt + l32] = dkacc[dt][r];
-        pk[(size_t)kBwdKeys * D + kl * D + 32 * dt + l32] = dvacc[dt][r];
-      }
-    return;
-  }
-  // partial dK / dV of this chunk (where the N sequences' prompt gradients
-  // meet); keys past the tile end add exact zeros to the tile's last key
-  if (kw < it.ke) {
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      float* dkp = dk_acc + (size_t)g * D + 32 * dt + l32;
-      float* dvp = dv_acc + (size_t)g * D + 32 * dt + l32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kk = kw + 8 * (r >> 2) + 4 * hl + (r & 3);
-        const size_t off = (size_t)min(kk, it.ke - 1) * krow;
-        const bool ok = kk < it.ke;
-        unsafeAtomicAdd(dkp + off, ok ? dkacc[dt][r] : 0.f);
-        unsafeAtomicAdd(dvp + off, ok ? dvacc[dt][r] : 0.f);
-      }
+    int nq = cq, nh = ch;
+    advance(nq, nh);
+    step(st, cq, nq, nh, QA0, OA0, LD0, QA1, OA1, LD1);
+    cq = nq; ch = nh;
+    if (st + 1 < nsteps) {
+      advance(nq, nh);
+      step(st + 1, cq, nq, nh, QA1, OA1, LD1, QA0, OA0, LD0);
+      cq = nq; ch = nh;
     }
   }
+
+  store_dkv<D>(dkacc, dvacc, dk_acc, dv_acc, part, it, item_id, g, w, lane, Hkv);
 }
 
 // ------------------------------------------------------------- reduce --
@@ -365,7 +404,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(
 template <int D>
 __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
-    const u16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
+    const u16* __restrict__ dO, const float2* __restrict__ rs,
     u16* __restrict__ dQ, const FwdItem* __restrict__ items, const Region* __restrict__ regions,
     HeadMap hm, int T, int Hq, int Hkv, float c, float scale) {
   constexpr int NW = kDqWaves;
@@ -411,12 +450,12 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
       of[kk] = b.v;
     }
   }
-  const float lse2 = lse[(size_t)h * T + tc] * kLog2e;
-  const float dl = delta[(size_t)h * T + tc];
+  const float2 rst = rs[(size_t)h * T + tc];
+  const float nlse2 = rst.x, dl = rst.y;   // -LSE log2 e, D
   // complete these loads before the tile loop (see the forward-copy waits)
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) asm volatile("" ::"v"(qf[kk]), "v"(of[kk]));
-  asm volatile("" ::"v"(lse2), "v"(dl));
+  asm volatile("" ::"v"(nlse2), "v"(dl));
 
   f32x16 dqacc[NDT];
 #pragma unroll
@@ -509,21 +548,19 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 8 * (r >> 2) + 4 * hl + (r & 3);
-          const float p = fast_exp2(fmaf(sacc[r], c, -lse2));
+          const float p = fast_exp2(fmaf(sacc[r], c, nlse2));
           sacc[r] = (key > t || key >= ke) ? 0.f : p;
         }
       } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[r] = fast_exp2(fmaf(sacc[r], c, -lse2));
+        for (int r = 0; r < 16; ++r) sacc[r] = fast_exp2(fmaf(sacc[r], c, nlse2));
       }
-      bf16x8 pf[2];
-      pack2(sacc, pf[0], pf[1]);
       f32x16 dpacc = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) dpacc = mfma32(frag_ld(va + (kb2 * NKK + kk) * kFrag, lane), of[kk], dpacc);
       pipelined_mfma<NKK, 1, 4>();
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dpacc[r] = bf16_elem(pf[r >> 3], r & 7) * (dpacc[r] - dl);
+      for (int r = 0; r < 16; ++r) dpacc[r] = sacc[r] * (dpacc[r] - dl);   // dS from the fp32 P
       bf16x8 sf[2];
       pack2(dpacc, sf[0], sf[1]);
       if constexpr (kRow) {
@@ -589,7 +626,7 @@ static int stream_grid(size_t n4) {
 hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dO, void* dQ, void* dK,
                       void* dV, const BwdItem* items_dev, int n_items, const FwdItem* qitems_dev,
-                      const Region* qregions_dev, int n_qitems, float* delta, float* dk_acc, float* dv_acc, float* part,
+                      const Region* qregions_dev, int n_qitems, float2* rs, float* dk_acc, float* dv_acc, float* part,
                       const int* tile_off, const int* tile_items, int n_tiles, hipStream_t stream,
                       int phase_mask) {
   const size_t nk = (size_t)pb.T * pb.Hkv * pb.d;
@@ -600,10 +637,10 @@ hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const voi
     dim3 grid((unsigned)((lanes + 255) / 256));
     if (pb.d == 128)
       hipLaunchKernelGGL(pre_kernel<128>, grid, dim3(256), 0, stream, (const u16*)o,
-                         (const u16*)dO, delta, pb.T, pb.Hq);
+                         (const u16*)dO, lse, rs, pb.T, pb.Hq);
     else
       hipLaunchKernelGGL(pre_kernel<64>, grid, dim3(256), 0, stream, (const u16*)o,
-                         (const u16*)dO, delta, pb.T, pb.Hq);
+                         (const u16*)dO, lse, rs, pb.T, pb.Hq);
     if (!part) {
       hipLaunchKernelGGL(zero_kernel, dim3(stream_grid(nk / 4)), dim3(256), 0, stream,
                          (float4*)dk_acc, nk / 4);
@@ -618,11 +655,11 @@ hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const voi
     dim3 grid(headmap_grid(hm)), block(64 * kBwdWaves);
     if (pb.d == 128)
       hipLaunchKernelGGL((dkv_kernel<128>), grid, block, 0, stream, (const u16*)q,
-                         (const u16*)k, (const u16*)v, (const u16*)dO, lse, delta, dk_acc, dv_acc,
+                         (const u16*)k, (const u16*)v, (const u16*)dO, rs, dk_acc, dv_acc,
                          part, items_dev, hm, pb.T, pb.Hq, pb.Hkv, c);
     else
       hipLaunchKernelGGL((dkv_kernel<64>), grid, block, 0, stream, (const u16*)q,
-                         (const u16*)k, (const u16*)v, (const u16*)dO, lse, delta, dk_acc, dv_acc,
+                         (const u16*)k, (const u16*)v, (const u16*)dO, rs, dk_acc, dv_acc,
                          part, items_dev, hm, pb.T, pb.Hq, pb.Hkv, c);
   }
   // 8. dQ (query-stationary), written directly as bf16
@@ -631,11 +668,11 @@ hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const voi
     dim3 grid(headmap_grid(hm)), block(64 * kDqWaves);
     if (pb.d == 128)
       hipLaunchKernelGGL((dq_kernel<128>), grid, block, 0, stream, (const u16*)q, (const u16*)k,
-                         (const u16*)v, (const u16*)dO, lse, delta, (u16*)dQ, qitems_dev,
+                         (const u16*)v, (const u16*)dO, rs, (u16*)dQ, qitems_dev,
                          qregions_dev, hm, pb.T, pb.Hq, pb.Hkv, c, pb.scale);
     else
       hipLaunchKernelGGL((dq_kernel<64>), grid, block, 0, stream, (const u16*)q, (const u16*)k,
-                         (const u16*)v, (const u16*)dO, lse, delta, (u16*)dQ, qitems_dev,
+                         (const u16*)v, (const u16*)dO, rs, (u16*)dQ, qitems_dev,
                          qregions_dev, hm, pb.T, pb.Hq, pb.Hkv, c, pb.scale);
   }
   // 4. dK, dV to bf16: convert the accumulators, or reduce the partials in order

@@ -37,6 +37,11 @@ __device__ __forceinline__ void dma16s(const void* base, uint32_t voff, void* ld
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(m)
                : "memory", "m0");
 }
+__device__ __forceinline__ void dma4s(const void* base, uint32_t voff, void* lds_base) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(m)
+               : "memory", "m0");
+}
 __device__ __forceinline__ void dma4(const void* g, void* lds_base) {
   const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m) : "memory", "m0");
@@ -79,12 +84,6 @@ __device__ __forceinline__ f32x16 xpose_nat(bf16x8 a0, bf16x8 a1, int lane) {
 __device__ __forceinline__ void pack2(const f32x16& x, bf16x8& f0, bf16x8& f1) {
   f0 = pack_bf16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
   f1 = pack_bf16x8(x[8], x[9], x[10], x[11], x[12], x[13], x[14], x[15]);
-}
-
-__device__ __forceinline__ float bf16_elem(const bf16x8& f, int e) {
-  Frag x{f};
-  const uint32_t w = e < 2 ? x.u.x : e < 4 ? x.u.y : e < 6 ? x.u.z : x.u.w;
-  return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
 }
 
 // Row-major 32 x 128 bf16 tiles with an XOR swizzle ("row tiles"). Row r is
