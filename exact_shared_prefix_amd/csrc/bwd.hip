@@ -492,9 +492,12 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
 
   // copies of tile i: job f = w, w + NW, ...: tensor f / NTF, key block
   // (f / NKK) % 2, d chunk f % NKK; keys past the region end read its last key
+  // (wave-uniform base at key kb, KV head g, plus a 32-bit per-lane byte offset)
   auto stage = [&](int i, u16* ka, u16* va) {
     int kb, ke;
     tile_bounds(i, kb, ke);
+    const int lim = ke - 1 - kb;   // last key of the region, relative to kb
+    const size_t base = (size_t)kb * krow + (size_t)g * D;
 #pragma unroll
     for (int j = 0; j < NJOB / NW; ++j) {
       const int f = w + NW * j;
@@ -502,13 +505,13 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
       if (kRow && f < NTF) {
         // rows 4 kk .. 4 kk + 3 of K row tile kb2
         const int r = 4 * kk + (lane >> 4);
-        const int key = min(kb + 32 * kb2 + r, ke - 1);
-        const int chunk = (lane & 15) ^ row_swz(r);
-        dma16(k + (size_t)key * krow + (size_t)g * D + 8 * chunk, ka + f * kFrag);
+        const uint32_t chunk = (uint32_t)((lane & 15) ^ row_swz(r));
+        const uint32_t voff = 2u * ((uint32_t)min(32 * kb2 + r, lim) * (uint32_t)krow + 8u * chunk);
+        dma16s(k + base, voff, ka + f * kFrag);
       } else {
-        const int key = min(kb + 32 * kb2 + l32, ke - 1);
-        const u16* src = (f < NTF ? k : v) + (size_t)key * krow + (size_t)g * D + 16 * kk + 8 * hl;
-        dma16(src, (f < NTF ? ka : va) + (f % NTF) * kFrag);
+        const uint32_t voff =
+            2u * ((uint32_t)min(32 * kb2 + l32, lim) * (uint32_t)krow + 16u * kk + 8u * hl);
+        dma16s((f < NTF ? k : v) + base, voff, (f < NTF ? ka : va) + (f % NTF) * kFrag);
       }
     }
   };
