@@ -408,10 +408,11 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
     u16* __restrict__ dQ, const FwdItem* __restrict__ items, const Region* __restrict__ regions,
     HeadMap hm, int T, int Hq, int Hkv, float c, float scale) {
   constexpr int NW = kDqWaves;
-  constexpr int BK = 64;          // keys per tile
+  constexpr int NB = kDqBlocks;   // 32-key blocks per tile
+  constexpr int BK = 32 * NB;     // keys per tile
   constexpr int NKK = D / 16;
   constexpr int NDT = D / 32;
-  constexpr int NTF = 2 * NKK;    // K (or V) fragments per tile: 2 key blocks x NKK
+  constexpr int NTF = NB * NKK;   // K (or V) fragments per tile: NB key blocks x NKK
   constexpr int NJOB = 2 * NTF;   // copies per tile (K and V)
   static_assert(NJOB % NW == 0, "copies per wave");
   constexpr bool kRow = D == 128;   // K as row tiles, K^T by transposing reads
@@ -419,7 +420,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
   __shared__ __attribute__((aligned(16))) u16 KA1[NTF * kFrag];
   __shared__ __attribute__((aligned(16))) u16 VA0[NTF * kFrag];
   __shared__ __attribute__((aligned(16))) u16 VA1[NTF * kFrag];
-  __shared__ __attribute__((aligned(16))) u16 KT[kRow ? 8 : 2 * NDT * 2 * kFrag];   // [kb2][dt][ks], d = 64
+  __shared__ __attribute__((aligned(16))) u16 KT[kRow ? 8 : NB * NDT * 2 * kFrag];   // [kb2][dt][ks], d = 64
 
   int item_id, h;
   if (!headmap_decode(hm, blockIdx.x, item_id, h)) return;
@@ -491,7 +492,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
   };
 
   // copies of tile i: job f = w, w + NW, ...: tensor f / NTF, key block
-  // (f / NKK) % 2, d chunk f % NKK; keys past the region end read its last key
+  // (f / NKK) % NB, d chunk f % NKK; keys past the region end read its last key
   // (wave-uniform base at key kb, KV head g, plus a 32-bit per-lane byte offset)
   auto stage = [&](int i, u16* ka, u16* va) {
     int kb, ke;
@@ -501,7 +502,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
 #pragma unroll
     for (int j = 0; j < NJOB / NW; ++j) {
       const int f = w + NW * j;
-      const int kb2 = (f / NKK) % 2, kk = f % NKK;
+      const int kb2 = (f / NKK) % NB, kk = f % NKK;
       if (kRow && f < NTF) {
         // rows 4 kk .. 4 kk + 3 of K row tile kb2
         const int r = 4 * kk + (lane >> 4);
@@ -523,7 +524,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
     if (i + 1 < ntiles) stage(i + 1, kan, van);
     // K^T A fragments (lane -> d, k-slots in accumulator key order)
 #pragma unroll
-    for (int p = w; !kRow && p < 2 * NDT; p += NW) {
+    for (int p = w; !kRow && p < NB * NDT; p += NW) {
       const int kb2 = p / NDT, dt = p % NDT;
       bf16x8 f0, f1;
       pack2(xpose_nat(frag_ld(ka + (kb2 * NKK + 2 * dt) * kFrag, lane),
@@ -535,7 +536,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
     if (!kRow) lds_barrier();
     if (!wave_rows) return;
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
+    for (int kb2 = 0; kb2 < NB; ++kb2) {
       const int k0 = kb + 32 * kb2;   // first key of this 32-key block
       if (k0 > t0 + 31 || k0 >= ke) continue;
       // S^T[key][query]: register r <-> key k0 + 8 (r/4) + 4 hl + r%4
@@ -545,6 +546,12 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
         sacc = mfma32(kRow ? row_ld_a(ka + kb2 * NKK * kFrag, abase ^ (32 * kk))
                            : frag_ld(ka + (kb2 * NKK + kk) * kFrag, lane),
                       qf[kk], sacc);
+      pipelined_mfma<NKK, 1, 4>();
+      // dP^T does not depend on P: its products go first, so the exponentials
+      // below overlap the end of the chain
+      f32x16 dpacc = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) dpacc = mfma32(frag_ld(va + (kb2 * NKK + kk) * kFrag, lane), of[kk], dpacc);
       pipelined_mfma<NKK, 1, 4>();
       const bool need_mask = (k0 + 31 > t0) || (k0 + 32 > ke);
       if (need_mask) {
@@ -558,10 +565,6 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[r] = fast_exp2(fmaf(sacc[r], c, nlse2));
       }
-      f32x16 dpacc = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) dpacc = mfma32(frag_ld(va + (kb2 * NKK + kk) * kFrag, lane), of[kk], dpacc);
-      pipelined_mfma<NKK, 1, 4>();
 #pragma unroll
       for (int r = 0; r < 16; ++r) dpacc[r] = sacc[r] * (dpacc[r] - dl);   // dS from the fp32 P
       bf16x8 sf[2];

@@ -61,8 +61,10 @@ constexpr int kFwdRows = 32 * kFwdWaves;
 // dK/dV workgroup: kBwdWaves waves of 32 keys each.
 constexpr int kBwdWaves = 8;
 constexpr int kBwdKeys = 32 * kBwdWaves;
-// dQ workgroup: kDqWaves waves of 32 query rows.
+// dQ workgroup: kDqWaves waves of 32 query rows; K / V tiles of kDqBlocks
+// 32-key blocks.
 constexpr int kDqWaves = 8;
+constexpr int kDqBlocks = 2;
 constexpr int kDqRows = 32 * kDqWaves;
 
 // Launch-time block -> (item, head) decomposition that keeps each head group
