@@ -110,8 +110,9 @@ __device__ __forceinline__ void store_dkv(const f32x16* dkacc, const f32x16* dva
   }
 }
 
-// Wave w owns keys kb + 32 w .. + 31: V fragments and the dK, dV accumulators
-// in registers, K fragments in its own LDS slots. Per 32-row step (query rows
+// Wave w owns keys kb + 32 w .. + 31: V fragments, half of the K fragments
+// (d = 128) and the dK, dV accumulators in registers, the other K fragments in
+// its own LDS slots. Per 32-row step (query rows
 // qb.., head h):
 //   S = Q K^T, P = exp2(S c - LSE log2 e), dP = dO V^T, dS = P (dP - D),
 //   dV += P^T dO, dK += dS^T Q.
@@ -164,9 +165,14 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
   const int nsteps = ((it.r1 - it.r0 + BQ - 1) / BQ) * G;
 
   // K, V fragments (lane -> key, 8 consecutive d); keys past the tile end
-  // read the tile's last key and are masked out of P
+  // read the tile's last key and are masked out of P. V and the first NKR K
+  // fragments stay in registers, the other K fragments in the wave's LDS slots
+  // (for d = 128 all of K would not fit in the 256 VGPRs of a wave beside the
+  // accumulators; for d = 64 it does).
+  constexpr int NKR = kRow ? NKK / 2 : NKK;
   u16* kfl = KF + w * NKK * kFrag;
   bf16x8 vf[NKK];
+  bf16x8 kf[NKR > 0 ? NKR : 1];
   {
     const int kc = min(key, it.ke - 1);
     const u16* kp = k + (size_t)kc * krow + (size_t)g * D + 8 * hl;
@@ -176,13 +182,21 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
       Frag b;
       b.u = *reinterpret_cast<const uint4*>(vp + 16 * kk);
       vf[kk] = b.v;
-      dma16(kp + 16 * kk, kfl + kk * kFrag);
+      if (kk < NKR) {
+        Frag a;
+        a.u = *reinterpret_cast<const uint4*>(kp + 16 * kk);
+        kf[kk < NKR ? kk : 0] = a.v;
+      } else {
+        dma16(kp + 16 * kk, kfl + kk * kFrag);
+      }
     }
   }
-  // complete the V loads here, so that no wait for them lands inside the step
-  // loop (where it would also wait for the copies in flight)
+  // complete the V, K loads here, so that no wait for them lands inside the
+  // step loop (where it would also wait for the copies in flight)
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) asm volatile("" ::"v"(vf[kk]));
+#pragma unroll
+  for (int kk = 0; kk < NKR; ++kk) asm volatile("" ::"v"(kf[kk]));
 
   f32x16 dkacc[NDT], dvacc[NDT];
 #pragma unroll
@@ -248,7 +262,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk)
         sacc = mfma32(kRow ? row_ld_a(qa, abase ^ (32 * kk)) : frag_ld(qa + kk * kFrag, lane),
-                      frag_ld(kfl + kk * kFrag, lane), sacc);
+                      kk < NKR ? kf[kk < NKR ? kk : 0] : frag_ld(kfl + kk * kFrag, lane), sacc);
       pipelined_mfma<NKK, 2, 2>();
       const float* lw = ld + 64 * w;
       if ((kw + 31 > qb) || (kw + 32 > it.ke) || (qb + BQ > it.r1)) {
