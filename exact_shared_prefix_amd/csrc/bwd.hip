@@ -305,6 +305,10 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
         }
       }
       pack2(dpacc, sf[0], sf[1]);
+      // dS complete before the dV, dK products: with its registers free the
+      // B-fragment reads of those products are issued an MFMA ahead (mixed
+      // in with the dS arithmetic, each product waited for its own reads)
+      sched_fence();
     }
     if (!active && st + 1 < nsteps) stage(nq, g * G + nh, qan, oan, ldn);
 
