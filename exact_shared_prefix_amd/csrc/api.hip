@@ -1,8 +1,8 @@
 // C ABI: argument checks, packed-layout descriptors, work lists, launches.
 //
-// The packed layout is the DualKV one (p2 abstract: P + NR tokens per
-// micro-batch; p1 "Approach": a shared-context KV region and per-sequence
-// response KV regions). Work lists are built on the host and copied into the
+// The packed layout is the DualKV one (arXiv abstract: P + NR tokens per
+// micro-batch; research-map summary, section Approach: a shared-context KV
+// region and per-sequence response KV regions). Work lists are built on the host and copied into the
 // caller's workspace on the caller's stream through pinned staging buffers;
 // no device memory is allocated here.
 #include <algorithm>
@@ -317,7 +317,7 @@ FwdLayout fwd_layout(const Problem& pb, size_t n_items, size_t n_regions, size_t
 }
 
 struct BwdLayout {
-  size_t items, qitems, qregions, delta, dk, dv, part, tile_off, tile_items, total;
+  size_t items, qitems, qregions, rowstat, dk, dv, part, tile_off, tile_items, total;
 };
 
 // Atomic mode: fp32 dK, dV accumulators [T][Hkv][d]. Deterministic mode:
@@ -329,7 +329,7 @@ BwdLayout bwd_layout(const Problem& pb, size_t n_items, size_t n_qitems, size_t 
   L.items = off;    off = align_up(off + n_items * sizeof(BwdItem));
   L.qitems = off;   off = align_up(off + n_qitems * sizeof(FwdItem));
   L.qregions = off; off = align_up(off + std::max<size_t>(1, n_qregions) * sizeof(Region));
-  L.delta = off;  off = align_up(off + (size_t)pb.Hq * pb.T * 2 * sizeof(float));   // {-LSE log2 e, D}
+  L.rowstat = off; off = align_up(off + (size_t)pb.Hq * pb.T * 2 * sizeof(float));   // {-LSE log2 e, D}
   if (det) {
     L.part = off;       off = align_up(off + n_items * pb.Hkv * 2 * (size_t)kBwdKeys * pb.d * sizeof(float));
     L.tile_off = off;   off = align_up(off + (n_tiles + 1) * sizeof(int));
@@ -428,7 +428,7 @@ dualkv_status bwd_impl(Problem& pb, const void* q, const void* k, const void* v,
   if (launch_bwd(pb, q, k, v, o, lse, dO, dQ, dK, dV, reinterpret_cast<const BwdItem*>(ws + L.items),
                  (int)items.size(), reinterpret_cast<const FwdItem*>(ws + L.qitems),
                  reinterpret_cast<const Region*>(ws + L.qregions), (int)qitems.size(),
-                 reinterpret_cast<float2*>(ws + L.delta),
+                 reinterpret_cast<float2*>(ws + L.rowstat),
                  det ? nullptr : reinterpret_cast<float*>(ws + L.dk),
                  det ? nullptr : reinterpret_cast<float*>(ws + L.dv),
                  det ? reinterpret_cast<float*>(ws + L.part) : nullptr,

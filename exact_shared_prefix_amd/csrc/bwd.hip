@@ -1,10 +1,12 @@
 // Backward kernels for shared-prompt attention.
 //
-// DualKV pages (p1 "Approach"): the backward walks the same two disjoint KV
-// regions as the forward, and the shared prompt's key/value gradients are
-// accumulated over all N sequences with fp32 atomics. Here:
-//  1. pre_kernel:  D_t = sum_d dO_t * O_t (fp32); zero_kernel clears the fp32
-//                  dK, dV accumulators.
+// "DualKV: Shared-Prompt Flash Attention for Efficient RL Training with Large
+// Rollouts and Long Contexts" (research-map summary, section Approach): the
+// backward walks the same two disjoint KV regions as the forward, and the
+// shared prompt's key/value gradients are accumulated over all N sequences
+// with fp32 atomics. Here:
+//  1. pre_kernel:  D_t = sum_d dO_t * O_t (fp32), stored beside -LSE_t log2 e;
+//                  zero_kernel clears the fp32 dK, dV accumulators.
 //  2. dkv_kernel:  key-stationary dK, dV. A workgroup owns 256 keys of one KV
 //                  head (8 waves x 32 keys) and walks the query rows that
 //                  attend them in 32-row steps, for each of the G query heads

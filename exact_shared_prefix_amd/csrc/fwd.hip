@@ -1,6 +1,6 @@
 // Forward kernel: shared-prompt attention over two KV regions in one launch.
 //
-// DualKV pages (p1 "Approach", p2 abstract): a tiled flash-attention forward
+// DualKV research-map summary (section Approach) and arXiv abstract: a tiled flash-attention forward
 // whose query tile walks the shared prompt's KV region and then its own
 // response's KV region, keeping one online-softmax state across both.
 //

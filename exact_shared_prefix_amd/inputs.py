@@ -4,8 +4,8 @@ This module only describes workloads and draws random numbers. It holds none of
 the attention arithmetic, so both the CPU oracle (test infrastructure) and the
 HIP path can consume what it produces without sharing any computation.
 
-Workloads follow the packed micro-batch of the DualKV pages (abstract, p2: one
-shared prompt of P tokens followed by N responses, P+NR tokens instead of
+Workloads follow the packed micro-batch of the DualKV pages (the arXiv abstract:
+one shared prompt of P tokens followed by N responses, P+NR tokens instead of
 N(P+R)); the head shapes are the Qwen3-8B ones the pages' GRPO runs use.
 
 Random numbers: every tensor is split into fixed-size chunks; chunk c of tensor

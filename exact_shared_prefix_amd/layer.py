@@ -1,6 +1,6 @@
 """A packed decoder layer around the shared-prompt attention (random weights).
 
-The DualKV abstract (p2) extends the token saving from attention to the whole
+The DualKV arXiv abstract extends the token saving from attention to the whole
 model: in a decoder-only model causal masking makes the prompt's hidden states
 identical across the N sequences at every layer, so the per-token operations
 (norms, projections, MLP) can process the prompt once, on P + sum(R_n) packed

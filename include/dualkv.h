@@ -1,7 +1,11 @@
 /*
  * dualkv.h -- C ABI of the MI355X (gfx950) shared-prompt attention library.
  *
- * The operation (DualKV pages: p1 "Approach", p2 abstract, p3 body): one
+ * The operation (DualKV pages: the research-map summary "DualKV: Shared-Prompt
+ * Flash Attention for Efficient RL Training with Large Rollouts and Long
+ * Contexts", section Approach; the arXiv abstract of that paper; the forum
+ * topic "DualKV: Eliminating N-fold Prompt Recomputation in RL Training of
+ * LLMs", its body): one
  * micro-batch is packed as a shared prompt of P tokens followed by N
  * responses, [prompt][resp_0]...[resp_{N-1}], T = P + sum_n R_n tokens instead
  * of N(P + R). With o_0 = P and o_{n+1} = o_n + R_n, packed row t attends
@@ -80,7 +84,8 @@ size_t dualkv_fwd_workspace_bytes(int P, int R, int N, const int32_t* offsets,
 size_t dualkv_bwd_workspace_bytes(int P, int R, int N, const int32_t* offsets,
                                   int Hq, int Hkv, int d, int deterministic);
 
-/* Forward pass (DualKV pages, p1 "Approach" / p2 abstract: one launch that
+/* Forward pass (research-map summary, section Approach, and the arXiv
+ * abstract: one launch that
  * walks the prompt KV region and then the row's own response KV region).
  * Reads q, k, v; writes o (bf16) and lse (fp32, natural log), and the V^T
  * fragments into the workspace (two launches on `stream`). */
@@ -89,7 +94,8 @@ dualkv_status dualkv_fwd(const void* q, const void* k, const void* v, void* o, f
                          int Hq, int Hkv, int d, float softmax_scale,
                          void* workspace, size_t workspace_bytes, void* stream);
 
-/* Backward pass of L = sum_t <dO_t, O_t> (p1 "Approach": gradients of the
+/* Backward pass of L = sum_t <dO_t, O_t> (research-map summary, section
+ * Approach: gradients of the
  * shared prompt accumulated across all N sequences with fp32 atomics).
  * Reads q, k, v, o, lse (from dualkv_fwd on the same inputs) and dO; writes
  * dQ, dK, dV (bf16). deterministic = 0 adds the row-chunk partials of dK and

@@ -11,7 +11,8 @@ Two independent formulations of the same definition live here:
   causal sequences [prompt; response_n], each is run through textbook softmax
   attention and its textbook backward, and the results are gathered back into
   the packed layout, summing the N copies' prompt gradients. This is what the
-  DualKV pages (abstract on p2; "Approach" on p1) say the fused kernels are
+  DualKV pages (the arXiv abstract; the research-map summary, section
+  Approach) say the fused kernels are
   exactly equivalent to.
 * ``sampled`` -- the packed definition written out per query row and per key:
   row t attends A(t) = {0..t} for a prompt row and {0..P-1} u {o_n..t} for a row

@@ -1,7 +1,7 @@
 """Float64 reference of one decoder layer on replicated sequences. TEST
 INFRASTRUCTURE ONLY.
 
-The DualKV abstract (p2): in a decoder-only model causal masking makes the
+The DualKV arXiv abstract: in a decoder-only model causal masking makes the
 prompt's hidden states identical across the N sequences at every layer, so
 every per-token operation can run on the packed P + sum(R_n) tokens. The
 reference here does the opposite, literally: it runs the layer on each

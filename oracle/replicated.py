@@ -1,10 +1,10 @@
 """Literal replicated-prompt oracle (float64, numpy). TEST INFRASTRUCTURE ONLY.
 
 Follows the DualKV pages: the method is exactly standard attention on N
-separate sequences [prompt; response_n] (p2 abstract: "mathematically
-equivalent to standard attention", the packing of N(P+R) tokens into P+NR;
-p1 "Approach": two disjoint KV regions, shared-prompt gradients accumulated
-across the N sequences). The oracle therefore does the replicated computation
+separate sequences [prompt; response_n] (the arXiv abstract of "DualKV":
+no approximation against standard attention, N(P+R) tokens packed into P+NR;
+the research-map summary of the same paper, section Approach: two disjoint KV
+regions, shared-prompt gradients accumulated across the N sequences). The oracle therefore does the replicated computation
 literally and only then folds it back to the packed layout.
 
 Readings taken where the pages are silent:

@@ -2,8 +2,8 @@
 
 At full workload sizes the literal replication is too slow to run whole, so
 this module evaluates the same definition directly on the packed layout for a
-chosen set of query rows or keys. The definition (DualKV pages, p1 "Approach"
-and p2 abstract): a prompt row t attends the prompt keys 0..t; a row t of
+chosen set of query rows or keys. The definition (the DualKV research-map
+summary, section Approach, and the arXiv abstract): a prompt row t attends the prompt keys 0..t; a row t of
 response n (o_n <= t < o_{n+1}) attends every prompt key and the keys o_n..t of
 its own response; nothing else. The loss is L = sum_{t,h} <dO_{t,h}, O_{t,h}>.
 
