@@ -24,7 +24,9 @@ typedef __attribute__((address_space(1))) const void glb_void;
 // as possibly overwritten by the copy (it would wait for all outstanding
 // memory operations before each one); the kernel waits for the copies itself.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+  // the low 32 bits of a generic pointer into LDS are its LDS address (the
+  // shared aperture's base has zero low bits); no null-pointer check needed
+  return (uint32_t)reinterpret_cast<uintptr_t>(p);
 }
 __device__ __forceinline__ void dma16(const void* g, void* lds_base) {
   const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
@@ -34,6 +36,12 @@ __device__ __forceinline__ void dma16(const void* g, void* lds_base) {
 // offset (no per-lane 64-bit address arithmetic).
 __device__ __forceinline__ void dma16s(const void* base, uint32_t voff, void* lds_base) {
   const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(m)
+               : "memory", "m0");
+}
+// Same as dma16s with the LDS destination given as an LDS byte address.
+__device__ __forceinline__ void dma16sl(const void* base, uint32_t voff, uint32_t lds) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds);
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(m)
                : "memory", "m0");
 }

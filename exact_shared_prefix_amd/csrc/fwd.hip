@@ -164,24 +164,30 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void fwd_kernel(
     int kb, ke;
     tile_bounds(i, kb, ke);
     const u16* base = k + (size_t)kb * krow + (size_t)g * D;
+    // the buffer's LDS address, materialised here rather than kept live (as
+    // one register per copy) across the loop
+    uint32_t l0 = lds_addr(dst);
+    asm volatile("" : "+s"(l0));
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
       const int f = (w - NL) + NL * j;
       const int kb2 = f / NKK, kk = f % NKK;
       const uint32_t row = (uint32_t)min(32 * kb2 + l32, ke - 1 - kb);
-      dma16s(base, 2u * (row * (uint32_t)krow + 16 * kk + 8 * hl), dst + f * kFrag);
+      dma16sl(base, 2u * (row * (uint32_t)krow + 16 * kk + 8 * hl), l0 + 2u * f * kFrag);
     }
   };
   auto copy_vt = [&](int i, u16* dst) __attribute__((always_inline)) {
     int kb, ke, b0;
     tile_region(i, kb, ke, b0);
     const int blast = b0 + (ke - 1 - kb) / 32;
+    uint32_t l0 = lds_addr(dst);
+    asm volatile("" : "+s"(l0));
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
       const int f = (w - NL) + NL * j;
       const int blk = min(b0 + f / (2 * NDT), blast);
       const u16* base = vt + ((size_t)blk * Hkv + g) * (2 * NDT * kFrag);
-      dma16s(base, 2u * ((f % (2 * NDT)) * kFrag + 8 * lane), dst + f * kFrag);
+      dma16sl(base, 2u * ((f % (2 * NDT)) * kFrag + 8 * lane), l0 + 2u * f * kFrag);
     }
   };
   // products of step j: S^T of tile j, then O^T += V^T P^T of tile j - 1
