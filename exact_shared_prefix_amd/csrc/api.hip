@@ -23,7 +23,7 @@ hipError_t launch_xpose_kv(const Problem& pb, const void* src, void* dst, const 
 hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dO, void* dQ, void* dK,
                       void* dV, const BwdItem* items_dev, int n_items, const FwdItem* qitems_dev,
-                      const Region* qregions_dev, int n_qitems, float2* rs, float* dk_acc,
+                      const Region* qregions_dev, int n_qitems, int max_qregions, float2* rs, float* dk_acc,
                       float* dv_acc, float* part,
                       const int* tile_off, const int* tile_items, int n_tiles, hipStream_t stream,
                       int phase_mask);
@@ -425,9 +425,11 @@ dualkv_status bwd_impl(Problem& pb, const void* q, const void* k, const void* v,
       (upload(ws + L.qitems, qitems.data(), qitems.size() * sizeof(FwdItem), s) != hipSuccess ||
        upload(ws + L.qregions, qregs.data(), qregs.size() * sizeof(Region), s) != hipSuccess))
     return DUALKV_ERR_HIP;
+  int max_qregions = 1;
+  for (const FwdItem& it : qitems) max_qregions = std::max(max_qregions, it.n_reg);
   if (launch_bwd(pb, q, k, v, o, lse, dO, dQ, dK, dV, reinterpret_cast<const BwdItem*>(ws + L.items),
                  (int)items.size(), reinterpret_cast<const FwdItem*>(ws + L.qitems),
-                 reinterpret_cast<const Region*>(ws + L.qregions), (int)qitems.size(),
+                 reinterpret_cast<const Region*>(ws + L.qregions), (int)qitems.size(), max_qregions,
                  reinterpret_cast<float2*>(ws + L.rowstat),
                  det ? nullptr : reinterpret_cast<float*>(ws + L.dk),
                  det ? nullptr : reinterpret_cast<float*>(ws + L.dv),

@@ -421,7 +421,9 @@ __global__ __launch_bounds__(256) void reduce_kernel(
 // the dQ product; for d = 64, K arrives as A fragments and K^T is made from
 // them by MFMA transposes.
 
-template <int D>
+// NR: the most key regions any item has (2 for one prompt level, up to
+// kMaxRegions).
+template <int D, int NR>
 __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const u16* __restrict__ dO, const float2* __restrict__ rs,
@@ -484,22 +486,23 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
 
   // key regions of the item (ancestor segments, then its own up to r1), kept in
   // scalar registers; tile i of the item is tile i - tbeg[x] of region x
-  int rk0[kMaxRegions], rk1[kMaxRegions], rblk[kMaxRegions], tbeg[kMaxRegions + 1];
+  static_assert(NR >= 1 && NR <= kMaxRegions, "region count");
+  int rk0[NR], rk1[NR], rblk[NR], tbeg[NR + 1];
   tbeg[0] = 0;
 #pragma unroll
-  for (int x = 0; x < kMaxRegions; ++x) {
+  for (int x = 0; x < NR; ++x) {
     const Region rg = x < it.n_reg ? regions[it.reg_off + x] : Region{0, 0, 0};
     rk0[x] = rg.k0;
     rk1[x] = rg.k1;
     rblk[x] = rg.blk;
     tbeg[x + 1] = tbeg[x] + (rg.k1 - rg.k0 + BK - 1) / BK;
   }
-  const int ntiles = tbeg[kMaxRegions];
+  const int ntiles = tbeg[NR];
   // tile i: keys [kb, ke) of its region (ke = region end), b0 = its first block
   auto tile_region = [&](int i, int& kb, int& ke, int& b0) __attribute__((always_inline)) {
     kb = 0; ke = 0; b0 = 0;
 #pragma unroll
-    for (int x = 0; x < kMaxRegions; ++x)
+    for (int x = 0; x < NR; ++x)
       if (i >= tbeg[x] && i < tbeg[x + 1]) {
         kb = rk0[x] + (i - tbeg[x]) * BK;
         ke = rk1[x];
@@ -652,7 +655,7 @@ static int stream_grid(size_t n4) {
 hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dO, void* dQ, void* dK,
                       void* dV, const BwdItem* items_dev, int n_items, const FwdItem* qitems_dev,
-                      const Region* qregions_dev, int n_qitems, float2* rs, float* dk_acc, float* dv_acc, float* part,
+                      const Region* qregions_dev, int n_qitems, int max_qregions, float2* rs, float* dk_acc, float* dv_acc, float* part,
                       const int* tile_off, const int* tile_items, int n_tiles, hipStream_t stream,
                       int phase_mask) {
   const size_t nk = (size_t)pb.T * pb.Hkv * pb.d;
@@ -692,14 +695,12 @@ hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const voi
   if ((phase_mask & 8) && n_qitems > 0) {
     HeadMap hm = make_headmap(n_qitems, pb.Hq);
     dim3 grid(headmap_grid(hm)), block(64 * kDqWaves);
-    if (pb.d == 128)
-      hipLaunchKernelGGL((dq_kernel<128>), grid, block, 0, stream, (const u16*)q, (const u16*)k,
-                         (const u16*)v, (const u16*)dO, rs, (u16*)dQ, qitems_dev,
-                         qregions_dev, hm, pb.T, pb.Hq, pb.Hkv, c, pb.scale);
-    else
-      hipLaunchKernelGGL((dq_kernel<64>), grid, block, 0, stream, (const u16*)q, (const u16*)k,
-                         (const u16*)v, (const u16*)dO, rs, (u16*)dQ, qitems_dev,
-                         qregions_dev, hm, pb.T, pb.Hq, pb.Hkv, c, pb.scale);
+    const bool deep = max_qregions > 2;
+    auto kern = pb.d == 128 ? (deep ? dq_kernel<128, kMaxRegions> : dq_kernel<128, 2>)
+                            : (deep ? dq_kernel<64, kMaxRegions> : dq_kernel<64, 2>);
+    hipLaunchKernelGGL(kern, grid, block, 0, stream, (const u16*)q, (const u16*)k, (const u16*)v,
+                       (const u16*)dO, rs, (u16*)dQ, qitems_dev, qregions_dev, hm, pb.T, pb.Hq,
+                       pb.Hkv, c, pb.scale);
   }
   // 4. dK, dV to bf16: convert the accumulators, or reduce the partials in order
   if (phase_mask & 4) {
