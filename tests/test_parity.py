@@ -87,6 +87,11 @@ SMALL = {
     # small N with a long prompt and short responses (the sweep's crossover regime)
     "small_n2_long_prompt": dict(P=1000, lengths=[37, 64], Hq=4, Hkv=2, d=128, seed=28),
     "n1_prompt_only_response": dict(P=777, lengths=[1], Hq=2, Hkv=1, d=128, seed=29),
+    # many tiny responses (0 .. 40 tokens): dozens of short regions, work items and tail masks
+    "many_tiny_responses_n40": dict(P=96, lengths=[(7 * i) % 41 for i in range(40)], Hq=8, Hkv=2,
+                                    d=128, seed=30),
+    # every region boundary on a 256-row / 256-key tile edge
+    "tile_aligned_p256_r256": dict(P=256, lengths=[256, 256], Hq=2, Hkv=1, d=128, seed=33),
 }
 
 
