@@ -200,7 +200,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void fwd_kernel(
       for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) s[kb2] = mfma32(frag_ld(ka + (kb2 * NKK + kk) * kFrag, lane), qf[kk], s[kb2]);
-      pipelined_mfma<2 * NKK, 1, 4>();
+      pipelined_mfma<2 * NKK, 1, 2>();
     }
     if (j > 0) {
 #pragma unroll
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void fwd_kernel(
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt)
             oacc[dt] = mfma32(frag_ld(vt_prev + ((kb2 * NDT + dt) * 2 + ks) * kFrag, lane), pf[kb2][ks], oacc[dt]);
-      pipelined_mfma<4 * NDT, 1, 4>();
+      pipelined_mfma<4 * NDT, 1, 2>();
     }
     __builtin_amdgcn_s_setprio(0);
   };
