@@ -79,7 +79,7 @@ def replicated_inputs(q, k, v, do, P, lengths):
             do.index_select(0, idx), [P + r for r in lengths])
 
 
-def time_steps(q, k, v, do, pk, scale, steps, warmup, phase_events=True):
+def time_steps(q, k, v, do, pk, scale, steps, warmup, phase_events=True, deterministic=False):
     """Run warmup + timed fwd+bwd steps; returns timings in ms."""
     import torch
     from exact_shared_prefix_amd import binding
@@ -90,7 +90,8 @@ def time_steps(q, k, v, do, pk, scale, steps, warmup, phase_events=True):
     lse = torch.empty((Hq, pk.T), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     wsf = torch.empty(binding.fwd_workspace_bytes(pk, Hq, Hkv, d), dtype=torch.uint8, device=dev)
-    wsb = torch.empty(binding.bwd_workspace_bytes(pk, Hq, Hkv, d), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(binding.bwd_workspace_bytes(pk, Hq, Hkv, d, deterministic), dtype=torch.uint8,
+                      device=dev)
     stream = torch.cuda.current_stream()
 
     phases = (binding.PHASE_PRE, binding.PHASE_MAIN, binding.PHASE_DQ, binding.PHASE_FINISH)
@@ -102,7 +103,8 @@ def time_steps(q, k, v, do, pk, scale, steps, warmup, phase_events=True):
         for i, ph in enumerate(phases):
             if ev:
                 ev[i + 1].record(stream)
-            binding.bwd(q, k, v, o, lse, do, pk, scale, dq, dk, dv, workspace=wsb, phases=ph)
+            binding.bwd(q, k, v, o, lse, do, pk, scale, dq, dk, dv, workspace=wsb,
+                        deterministic=deterministic, phases=ph)
         if ev:
             ev[5].record(stream)
 
@@ -505,6 +507,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-mfma-peak", action="store_true", help="skip the measured MFMA peak")
+    ap.add_argument("--no-deterministic", action="store_true",
+                    help="skip the deterministic-mode (two-pass prompt dK/dV reduction) timing")
     ap.add_argument("--layer", action="store_true",
                     help="one packed decoder layer (random weights) vs the replicated layout")
     ap.add_argument("--tree", action="store_true",
@@ -581,6 +585,22 @@ def main() -> int:
     other = {n: {"ms": kv["ms"], "tflops": kv["flops"] / (kv["ms"] * 1e-3) / 1e12}
              for n, kv in kernels.items()}
 
+    deterministic = None
+    if not args.no_deterministic:
+        # the same step with the prompt dK/dV summed by the ordered two-pass
+        # reduction (per-item partials, then reduce_kernel) instead of atomics
+        dsteps = max(2, args.steps // 3)
+        log(f"[bench] deterministic mode: 1 warmup + {dsteps} timed steps")
+        det = time_steps(q, k, v, do, pk, inp.scale, dsteps, 1, deterministic=True)
+        nws = binding.bwd_workspace_bytes(pk, inp.Hq, inp.Hkv, inp.d, True)
+        deterministic = {"ms_per_step": det["ms_per_step"],
+                         "bwd_dkv_ms": det["bwd_dkv_ms"], "bwd_reduce_ms": det["bwd_finish_ms"],
+                         "bwd_workspace_gb": nws / 1e9,
+                         "slowdown_vs_atomic": det["ms_per_step"] / ms}
+        log(f"[bench] deterministic: {det['ms_per_step']:.2f} ms/step (ordered reduction "
+            f"{det['bwd_finish_ms']:.2f} ms, workspace {nws / 1e9:.2f} GB)")
+        torch.cuda.empty_cache()
+
     replicated = None
     if not args.no_replicated:
         del q, k, v, do
@@ -649,6 +669,7 @@ def main() -> int:
         "roofline": roofline,
         "peak_hbm_gb": peak_packed / 1e9,
         "mfma_peak": mfma_peak,
+        "deterministic": deterministic,
         "replicated": replicated,
         "cpu_baseline": cpu,
     }
