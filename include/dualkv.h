@@ -77,8 +77,9 @@ size_t dualkv_fwd_workspace_bytes(int P, int R, int N, const int32_t* offsets,
                                   int Hq, int Hkv, int d);
 
 /* Workspace dualkv_bwd needs: the two work lists, the per-row pairs
- * {-LSE * log2(e), D = rowsum(dO*O)} [Hq][T] fp32, and either fp32 accumulators for dK and dV [T][Hkv][d] (atomic mode)
- * or, with deterministic != 0, per-work-item dK/dV partials plus the lists of
+ * {-LSE * log2(e), D = rowsum(dO*O)} [Hq][T] fp32, and either fp32
+ * accumulators for dK and dV [T][Hkv][d] (atomic mode) or, with
+ * deterministic != 0, per-work-item dK/dV partials plus the lists of
  * each key tile's items (dQ is written directly in both modes). 0 if the
  * arguments are invalid. */
 size_t dualkv_bwd_workspace_bytes(int P, int R, int N, const int32_t* offsets,
@@ -109,8 +110,9 @@ dualkv_status dualkv_bwd(const void* q, const void* k, const void* v, const void
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* The backward of dualkv_bwd split into its stream-ordered phases, so a
- * caller can time or interleave them: bit 1 = preprocess (D = rowsum(dO*O), paired with the base-2 LSE;
- * in atomic mode also zeroed fp32 dK, dV accumulators), bit 2 = key-stationary
+ * caller can time or interleave them: bit 1 = preprocess (D = rowsum(dO*O),
+ * paired with the base-2 LSE; in atomic mode also zeroed fp32 dK, dV
+ * accumulators), bit 2 = key-stationary
  * dK, dV pass (two KV regions; atomics into the accumulators, or partials in
  * deterministic mode), bit 8 = query-stationary dQ pass (writes dQ), bit 4 =
  * finish (accumulators -> bf16 dK, dV, or the ordered reduction of the
