@@ -2,9 +2,9 @@
 //
 // The packed layout is the DualKV one (arXiv abstract: P + NR tokens per
 // micro-batch; research-map summary, section Approach: a shared-context KV
-// region and per-sequence response KV regions). Work lists are built on the host and copied into the
-// caller's workspace on the caller's stream through pinned staging buffers;
-// no device memory is allocated here.
+// region and per-sequence response KV regions). Work lists are built on the
+// host and copied into the caller's workspace on the caller's stream through
+// pinned staging buffers; no device memory is allocated here.
 #include <algorithm>
 #include <cmath>
 #include <cstring>
@@ -23,8 +23,8 @@ hipError_t launch_xpose_kv(const Problem& pb, const void* src, void* dst, const 
 hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dO, void* dQ, void* dK,
                       void* dV, const BwdItem* items_dev, int n_items, const FwdItem* qitems_dev,
-                      const Region* qregions_dev, int n_qitems, int max_qregions, float2* rs, float* dk_acc,
-                      float* dv_acc, float* part,
+                      const Region* qregions_dev, int n_qitems, int max_qregions, float2* rs,
+                      float* dk_acc, float* dv_acc, float* part,
                       const int* tile_off, const int* tile_items, int n_tiles, hipStream_t stream,
                       int phase_mask);
 }  // namespace dkv
