@@ -7,6 +7,7 @@ call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional, Sequence
@@ -160,6 +161,26 @@ def _stream_ptr(stream) -> int:
     return s.cuda_stream
 
 
+def _alloc_on(stream):
+    """Context for the tensors a call allocates (outputs, workspace): they come
+    from the launch stream's pool, so the caching allocator cannot hand their
+    memory to other work before the kernels enqueued on that stream ran."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
+def _workspace(ws, nbytes: int, device):
+    """The caller's workspace if it is a contiguous uint8 tensor of at least
+    nbytes on `device`, else a fresh one (allocated under _alloc_on)."""
+    if ws is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if ws.dtype != torch.uint8 or not ws.is_contiguous() or ws.device != device:
+        raise ValueError(f"workspace: expected a contiguous uint8 tensor on {device}, got "
+                         f"{ws.dtype} on {ws.device}" + ("" if ws.is_contiguous() else " (strided)"))
+    if ws.numel() < nbytes:
+        raise ValueError(f"workspace: {ws.numel()} bytes, the call needs {nbytes}")
+    return ws
+
+
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
@@ -198,28 +219,64 @@ def bwd_workspace_bytes(pk: Packing, Hq: int, Hkv: int, d: int, deterministic: b
     return n
 
 
+def _fwd_common(q, k, v, T: int, scale, out, lse, workspace, stream, nws_fn):
+    """Checks and allocations shared by the forward wrappers; returns
+    (Hq, Hkv, d, scale, out, lse, workspace)."""
+    _, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    _check_tensor("q", q, (T, Hq, d), torch.bfloat16, dev)
+    _check_tensor("k", k, (T, Hkv, d), torch.bfloat16, dev)
+    _check_tensor("v", v, (T, Hkv, d), torch.bfloat16, dev)
+    scale = d ** -0.5 if scale is None else scale
+    nws = nws_fn(Hq, Hkv, d)
+    with _alloc_on(stream):
+        out = torch.empty_like(q) if out is None else out
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=dev) if lse is None else lse
+        workspace = _workspace(workspace, nws, dev)
+    _check_tensor("o", out, (T, Hq, d), torch.bfloat16, dev)
+    _check_tensor("lse", lse, (Hq, T), torch.float32, dev)
+    return Hq, Hkv, d, scale, out, lse, workspace
+
+
+def _bwd_common(q, k, v, o, lse, do, T: int, scale, dq, dk, dv, workspace, stream, nws_fn):
+    """Checks and allocations shared by the backward wrappers; returns
+    (Hq, Hkv, d, scale, dq, dk, dv, workspace)."""
+    _, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    for name, t, hh in (("q", q, Hq), ("o", o, Hq), ("do", do, Hq), ("k", k, Hkv), ("v", v, Hkv)):
+        _check_tensor(name, t, (T, hh, d), torch.bfloat16, dev)
+    _check_tensor("lse", lse, (Hq, T), torch.float32, dev)
+    scale = d ** -0.5 if scale is None else scale
+    nws = nws_fn(Hq, Hkv, d)
+    with _alloc_on(stream):
+        dq = torch.empty_like(q) if dq is None else dq
+        dk = torch.empty_like(k) if dk is None else dk
+        dv = torch.empty_like(v) if dv is None else dv
+        workspace = _workspace(workspace, nws, dev)
+    for name, t, hh in (("dq", dq, Hq), ("dk", dk, Hkv), ("dv", dv, Hkv)):
+        _check_tensor(name, t, (T, hh, d), torch.bfloat16, dev)
+    return Hq, Hkv, d, scale, dq, dk, dv, workspace
+
+
+def _cached_ws(cache: dict, key, query) -> int:
+    if key not in cache:
+        cache[key] = query()
+    n = cache[key]
+    if n == 0:
+        raise DualKVError(ERR_INVALID_ARG, "invalid problem shape")
+    return n
+
+
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pk: Packing,
         scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
         lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
         stream=None):
     """dualkv_fwd. q [T,Hq,d], k/v [T,Hkv,d] bf16 on the GPU -> (o, lse)."""
-    T, Hq, d = q.shape
-    Hkv = k.shape[1]
-    dev = q.device
-    _check_tensor("q", q, (pk.T, Hq, d), torch.bfloat16, dev)
-    _check_tensor("k", k, (pk.T, Hkv, d), torch.bfloat16, dev)
-    _check_tensor("v", v, (pk.T, Hkv, d), torch.bfloat16, dev)
-    if scale is None:
-        scale = d ** -0.5
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((Hq, pk.T), dtype=torch.float32, device=dev)
-    _check_tensor("o", out, (pk.T, Hq, d), torch.bfloat16, dev)
-    _check_tensor("lse", lse, (Hq, pk.T), torch.float32, dev)
-    nws = fwd_workspace_bytes(pk, Hq, Hkv, d)
-    if workspace is None or workspace.numel() < nws:
-        workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+    Hq, Hkv, d, scale, out, lse, workspace = _fwd_common(
+        q, k, v, pk.T, scale, out, lse, workspace, stream,
+        lambda Hq, Hkv, d: fwd_workspace_bytes(pk, Hq, Hkv, d))
     _check(load().dualkv_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), pk.P, pk.R, pk.N,
                              pk.offsets_ptr(), Hq, Hkv, d, float(scale), _ptr(workspace),
                              workspace.numel(), _stream_ptr(stream)))
@@ -235,20 +292,9 @@ def bwd(q, k, v, o, lse, do, pk: Packing, scale: Optional[float] = None,
     (dualkv_bwd_phases: PHASE_PRE, PHASE_MAIN (dK, dV), PHASE_DQ, PHASE_FINISH);
     the outputs are complete only once all of them ran on the same workspace,
     PHASE_PRE first and PHASE_MAIN before PHASE_FINISH."""
-    T, Hq, d = q.shape
-    Hkv = k.shape[1]
-    dev = q.device
-    for name, t, hh in (("q", q, Hq), ("o", o, Hq), ("do", do, Hq), ("k", k, Hkv), ("v", v, Hkv)):
-        _check_tensor(name, t, (pk.T, hh, d), torch.bfloat16, dev)
-    _check_tensor("lse", lse, (Hq, pk.T), torch.float32, dev)
-    if scale is None:
-        scale = d ** -0.5
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    nws = bwd_workspace_bytes(pk, Hq, Hkv, d, deterministic)
-    if workspace is None or workspace.numel() < nws:
-        workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+    Hq, Hkv, d, scale, dq, dk, dv, workspace = _bwd_common(
+        q, k, v, o, lse, do, pk.T, scale, dq, dk, dv, workspace, stream,
+        lambda Hq, Hkv, d: bwd_workspace_bytes(pk, Hq, Hkv, d, deterministic))
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
             pk.P, pk.R, pk.N, pk.offsets_ptr(), Hq, Hkv, d, float(scale), int(deterministic),
             _ptr(workspace), workspace.numel(), _stream_ptr(stream))
@@ -262,25 +308,10 @@ def bwd(q, k, v, o, lse, do, pk: Packing, scale: Optional[float] = None,
 def fwd_groups(q, k, v, gp: GroupPacking, scale: Optional[float] = None, out=None, lse=None,
                workspace=None, stream=None):
     """dualkv_fwd_groups -> (o, lse); layouts as fwd()."""
-    T, Hq, d = q.shape
-    Hkv = k.shape[1]
-    dev = q.device
-    _check_tensor("q", q, (gp.T, Hq, d), torch.bfloat16, dev)
-    _check_tensor("k", k, (gp.T, Hkv, d), torch.bfloat16, dev)
-    _check_tensor("v", v, (gp.T, Hkv, d), torch.bfloat16, dev)
-    scale = d ** -0.5 if scale is None else scale
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((Hq, gp.T), dtype=torch.float32, device=dev) if lse is None else lse
-    _check_tensor("o", out, (gp.T, Hq, d), torch.bfloat16, dev)
-    _check_tensor("lse", lse, (Hq, gp.T), torch.float32, dev)
-    key = ("fwd", Hq, Hkv, d)
-    if key not in gp._ws:
-        gp._ws[key] = load().dualkv_fwd_workspace_bytes_groups(*gp.args(), Hq, Hkv, d)
-    nws = gp._ws[key]
-    if nws == 0:
-        raise DualKVError(ERR_INVALID_ARG, "invalid problem shape")
-    if workspace is None or workspace.numel() < nws:
-        workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+    Hq, Hkv, d, scale, out, lse, workspace = _fwd_common(
+        q, k, v, gp.T, scale, out, lse, workspace, stream,
+        lambda Hq, Hkv, d: _cached_ws(gp._ws, ("fwd", Hq, Hkv, d),
+                                      lambda: load().dualkv_fwd_workspace_bytes_groups(*gp.args(), Hq, Hkv, d)))
     _check(load().dualkv_fwd_groups(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), *gp.args(),
                                     Hq, Hkv, d, float(scale), _ptr(workspace), workspace.numel(),
                                     _stream_ptr(stream)))
@@ -291,25 +322,11 @@ def bwd_groups(q, k, v, o, lse, do, gp: GroupPacking, scale: Optional[float] = N
                dq=None, dk=None, dv=None, workspace=None, deterministic: bool = False,
                stream=None):
     """dualkv_bwd_groups -> (dq, dk, dv); layouts as bwd()."""
-    T, Hq, d = q.shape
-    Hkv = k.shape[1]
-    dev = q.device
-    for name, t, hh in (("q", q, Hq), ("o", o, Hq), ("do", do, Hq), ("k", k, Hkv), ("v", v, Hkv)):
-        _check_tensor(name, t, (gp.T, hh, d), torch.bfloat16, dev)
-    _check_tensor("lse", lse, (Hq, gp.T), torch.float32, dev)
-    scale = d ** -0.5 if scale is None else scale
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    key = ("bwd", Hq, Hkv, d, bool(deterministic))
-    if key not in gp._ws:
-        gp._ws[key] = load().dualkv_bwd_workspace_bytes_groups(*gp.args(), Hq, Hkv, d,
-                                                               int(deterministic))
-    nws = gp._ws[key]
-    if nws == 0:
-        raise DualKVError(ERR_INVALID_ARG, "invalid problem shape")
-    if workspace is None or workspace.numel() < nws:
-        workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+    Hq, Hkv, d, scale, dq, dk, dv, workspace = _bwd_common(
+        q, k, v, o, lse, do, gp.T, scale, dq, dk, dv, workspace, stream,
+        lambda Hq, Hkv, d: _cached_ws(gp._ws, ("bwd", Hq, Hkv, d, bool(deterministic)),
+                                      lambda: load().dualkv_bwd_workspace_bytes_groups(
+                                          *gp.args(), Hq, Hkv, d, int(deterministic))))
     _check(load().dualkv_bwd_groups(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
                                     _ptr(dq), _ptr(dk), _ptr(dv), *gp.args(), Hq, Hkv, d,
                                     float(scale), int(deterministic), _ptr(workspace),
@@ -320,25 +337,10 @@ def bwd_groups(q, k, v, o, lse, do, gp: GroupPacking, scale: Optional[float] = N
 def fwd_tree(q, k, v, tp: TreePacking, scale: Optional[float] = None, out=None, lse=None,
              workspace=None, stream=None):
     """dualkv_fwd_tree -> (o, lse); layouts as fwd()."""
-    T, Hq, d = q.shape
-    Hkv = k.shape[1]
-    dev = q.device
-    _check_tensor("q", q, (tp.T, Hq, d), torch.bfloat16, dev)
-    _check_tensor("k", k, (tp.T, Hkv, d), torch.bfloat16, dev)
-    _check_tensor("v", v, (tp.T, Hkv, d), torch.bfloat16, dev)
-    scale = d ** -0.5 if scale is None else scale
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((Hq, tp.T), dtype=torch.float32, device=dev) if lse is None else lse
-    _check_tensor("o", out, (tp.T, Hq, d), torch.bfloat16, dev)
-    _check_tensor("lse", lse, (Hq, tp.T), torch.float32, dev)
-    key = ("fwd", Hq, Hkv, d)
-    if key not in tp._ws:
-        tp._ws[key] = load().dualkv_fwd_workspace_bytes_tree(*tp.args(), Hq, Hkv, d)
-    nws = tp._ws[key]
-    if nws == 0:
-        raise DualKVError(ERR_INVALID_ARG, "invalid problem shape")
-    if workspace is None or workspace.numel() < nws:
-        workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+    Hq, Hkv, d, scale, out, lse, workspace = _fwd_common(
+        q, k, v, tp.T, scale, out, lse, workspace, stream,
+        lambda Hq, Hkv, d: _cached_ws(tp._ws, ("fwd", Hq, Hkv, d),
+                                      lambda: load().dualkv_fwd_workspace_bytes_tree(*tp.args(), Hq, Hkv, d)))
     _check(load().dualkv_fwd_tree(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), *tp.args(),
                                   Hq, Hkv, d, float(scale), _ptr(workspace), workspace.numel(),
                                   _stream_ptr(stream)))
@@ -348,24 +350,11 @@ def fwd_tree(q, k, v, tp: TreePacking, scale: Optional[float] = None, out=None, 
 def bwd_tree(q, k, v, o, lse, do, tp: TreePacking, scale: Optional[float] = None,
              dq=None, dk=None, dv=None, workspace=None, deterministic: bool = False, stream=None):
     """dualkv_bwd_tree -> (dq, dk, dv); layouts as bwd()."""
-    T, Hq, d = q.shape
-    Hkv = k.shape[1]
-    dev = q.device
-    for name, t, hh in (("q", q, Hq), ("o", o, Hq), ("do", do, Hq), ("k", k, Hkv), ("v", v, Hkv)):
-        _check_tensor(name, t, (tp.T, hh, d), torch.bfloat16, dev)
-    _check_tensor("lse", lse, (Hq, tp.T), torch.float32, dev)
-    scale = d ** -0.5 if scale is None else scale
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    key = ("bwd", Hq, Hkv, d, bool(deterministic))
-    if key not in tp._ws:
-        tp._ws[key] = load().dualkv_bwd_workspace_bytes_tree(*tp.args(), Hq, Hkv, d, int(deterministic))
-    nws = tp._ws[key]
-    if nws == 0:
-        raise DualKVError(ERR_INVALID_ARG, "invalid problem shape")
-    if workspace is None or workspace.numel() < nws:
-        workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+    Hq, Hkv, d, scale, dq, dk, dv, workspace = _bwd_common(
+        q, k, v, o, lse, do, tp.T, scale, dq, dk, dv, workspace, stream,
+        lambda Hq, Hkv, d: _cached_ws(tp._ws, ("bwd", Hq, Hkv, d, bool(deterministic)),
+                                      lambda: load().dualkv_bwd_workspace_bytes_tree(
+                                          *tp.args(), Hq, Hkv, d, int(deterministic))))
     _check(load().dualkv_bwd_tree(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
                                   _ptr(dq), _ptr(dk), _ptr(dv), *tp.args(), Hq, Hkv, d,
                                   float(scale), int(deterministic), _ptr(workspace),

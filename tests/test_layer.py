@@ -38,10 +38,50 @@ def test_rope_preserves_norm_and_depends_on_relative_position():
     assert torch.equal(rope64(q, torch.tensor([0]), 1e4), q)
 
 
+def test_rope_frequency_schedule_closed_form():
+    """Rotary frequencies of the RoFormer / rotate-half convention: pair i of a
+    d-wide head (elements i and i + d/2) turns by pos * theta^(-2i/d). Pinned by
+    values with closed forms at theta = 10^4, d = 16: pair 0 turns by pos
+    radians, pair 1 by pos * 10^-0.5 (= pos / sqrt(10)), pair 7 = d/2 - 1 by
+    pos * 10^-3.5. A unit vector on element i must come out as
+    cos(a) e_i + sin(a) e_(i + d/2); theta^(-i/d) or theta^(-2(i+1)/d) would
+    move pair 1 to 10^-0.25 or 10^-1."""
+    d, theta = 16, 1.0e4
+    expect = {0: 1.0, 1: 1.0 / np.sqrt(10.0), 7: 10.0 ** -3.5}
+    for pos in (1, 3):
+        for i, f in expect.items():
+            x = torch.zeros(1, 1, d, dtype=torch.float64)
+            x[0, 0, i] = 1.0
+            y = rope64(x, torch.tensor([pos]), theta)[0, 0]
+            want = torch.zeros(d, dtype=torch.float64)
+            want[i] = np.cos(pos * f)
+            want[i + d // 2] = np.sin(pos * f)
+            assert torch.allclose(y, want, rtol=0, atol=1e-14), (pos, i, y, want)
+            # the partner element rotates the other way: e_(i + d/2) -> -sin e_i + cos e_(i + d/2)
+            x2 = torch.zeros(1, 1, d, dtype=torch.float64)
+            x2[0, 0, i + d // 2] = 1.0
+            y2 = rope64(x2, torch.tensor([pos]), theta)[0, 0]
+            want2 = torch.zeros(d, dtype=torch.float64)
+            want2[i] = -np.sin(pos * f)
+            want2[i + d // 2] = np.cos(pos * f)
+            assert torch.allclose(y2, want2, rtol=0, atol=1e-14), (pos, i)
+
+
 def test_rms_norm_unit_rms():
     x = torch.randn(5, 32, dtype=torch.float64) * 7
     y = rms_norm64(x, torch.ones(32, dtype=torch.float64), 0.0)
     assert torch.allclose(y.pow(2).mean(-1), torch.ones(5, dtype=torch.float64), rtol=1e-12)
+
+
+def test_rms_norm_weight_closed_form():
+    """x = 2 * (1, -1, 1, -1) has root mean square 2, so with eps = 0 the
+    normalised row is (1, -1, 1, -1) and the weight multiplies it elementwise;
+    eps = 12 makes the denominator sqrt(4 + 12) = 4."""
+    x = torch.tensor([[2.0, -2.0, 2.0, -2.0]], dtype=torch.float64)
+    w = torch.tensor([1.0, 2.0, 3.0, 4.0], dtype=torch.float64)
+    assert torch.equal(rms_norm64(x, w, 0.0), torch.tensor([[1.0, -2.0, 3.0, -4.0]], dtype=torch.float64))
+    assert torch.allclose(rms_norm64(x, w, 12.0), torch.tensor([[0.5, -1.0, 1.5, -2.0]], dtype=torch.float64),
+                          rtol=0, atol=1e-15)
 
 
 def _packed_mask(P, lengths):

@@ -92,6 +92,10 @@ SMALL = {
                                     d=128, seed=30),
     # every region boundary on a 256-row / 256-key tile edge
     "tile_aligned_p256_r256": dict(P=256, lengths=[256, 256], Hq=2, Hkv=1, d=128, seed=33),
+    # head counts that neither divide nor are multiples of 8: the launch's
+    # block -> (item, head) map takes its plain form (no XCD grouping)
+    "headmap_plain_h12_kv3_d128": dict(P=300, lengths=[200, 57, 0, 130], Hq=12, Hkv=3, d=128, seed=35),
+    "headmap_plain_h12_kv3_d64": dict(P=190, lengths=[70, 260, 1], Hq=12, Hkv=3, d=64, seed=36),
 }
 
 
@@ -182,6 +186,97 @@ def test_deterministic_mode_bitwise_repeat_multi_chunk():
     for key in ("dQ", "dK", "dV"):
         assert np.array_equal(a[key], b[key]), key
         assert rel(a[key], c[key]) <= 1e-3, key
+
+
+# ------------------------------------------------ across the row-chunk grid --
+# The dK/dV pass cuts every key tile's attending rows into 2048-row chunks; a
+# prompt key tile's gradient is the sum of the partials of all its chunks (fp32
+# atomics, or the ordered sum of the deterministic mode). These cases have
+# T > 4096, so prompt tiles span three or more chunks, and every element is
+# compared with the replicated oracle in both modes.
+CHUNKED = {
+    "chunks_p4096_gqa4_d128": dict(P=4096, lengths=[2500, 3000, 1800], Hq=8, Hkv=2, d=128, seed=34),
+    "chunks_p2400_ragged_d64": dict(P=2400, lengths=[1900, 1500, 700, 3], Hq=2, Hkv=1, d=64, seed=37),
+}
+_ORACLE_CACHE = {}
+
+
+def _chunked(name):
+    if name not in _ORACLE_CACHE:
+        kw = dict(CHUNKED[name])
+        P, lengths, Hq, Hkv, d, seed = (kw.pop(x) for x in ("P", "lengths", "Hq", "Hkv", "d", "seed"))
+        inp = make_inputs(P, lengths, Hq, Hkv, d, seed=seed)
+        say(f"case {name}: oracle for P={P} lengths={lengths} Hq={Hq} Hkv={Hkv} d={d}")
+        ref = oracle_fwd_bwd(np64(inp.q), np64(inp.k), np64(inp.v), np64(inp.do), P, lengths, inp.scale)
+        _ORACLE_CACHE[name] = (inp, ref)
+    return _ORACLE_CACHE[name]
+
+
+@pytest.mark.parametrize("det", [False, True])
+@pytest.mark.parametrize("name", sorted(CHUNKED))
+def test_across_row_chunks_elementwise(name, det):
+    inp, ref = _chunked(name)
+    assert inp.T > 2 * 2048
+    say(f"case {name} deterministic={det}: T={inp.T}")
+    got = run_gpu(inp, deterministic=det)
+    check_all(got, ref, inp.P, f"{name} det={det}")
+    # prompt keys per 256-key tile: every tile's multi-chunk sum on its own
+    for t0 in range(0, inp.P, 256):
+        t1 = min(inp.P, t0 + 256)
+        for key in ("dK", "dV"):
+            e = rel(got[key][t0:t1], ref[key][t0:t1])
+            assert e <= REL, (key, t0, e)
+
+
+def _plant_reference_moves(inp, plants):
+    """Make chosen rows' scores jump far above their first key tile: for
+    (row t, key j, alpha) set k_j = alpha * q_t (query head h = first of the
+    KV head's group, every KV head), so row t's score on key j is about
+    alpha * |q_t|^2 * scale (tens of log2 units for alpha >= 2, d = 128)."""
+    G = inp.Hq // inp.Hkv
+    k = inp.k.clone()
+    for t, j, alpha in plants:
+        for g in range(inp.Hkv):
+            k[j, g] = (alpha * inp.q[t, g * G].float()).to(torch.bfloat16)
+    inp.k = k
+    return inp
+
+
+def test_forward_reference_moves_elementwise():
+    """Rows whose scores rise by 20 to 60 log2 units after their first key
+    tile, once or twice along the row (inside the prompt region, at the switch
+    to the own-response region, and inside it), plus a key ramp that makes
+    later keys larger for every row: the forward must move its reference and
+    rescale O and the row sum, and the backward must agree."""
+    P, lengths = 400, [300, 200, 90]
+    inp = make_inputs(P, lengths, 4, 2, 128, seed=38)
+    o = [P] + list(P + np.cumsum(lengths))
+    plants = [
+        (300, 150, 2.0), (300, 290, 4.0),          # prompt row: two moves, in tiles 2 and 4
+        (o[0] + 10, 380, 2.5),                     # response row: late prompt tile
+        (o[0] + 250, o[0] + 200, 3.0),             # response row: inside its own region
+        (o[1] + 150, 70, 2.0), (o[1] + 150, o[1] + 140, 4.0),
+        (o[2] + 89, o[2] + 80, 3.5),
+    ]
+    _plant_reference_moves(inp, plants)
+    c = inp.scale * np.log2(np.e)
+    for t, j, _ in plants:
+        first = np.max(np64(inp.q)[t, 0] @ np64(inp.k)[:64, 0].T) * c
+        jump = float(np64(inp.q)[t, 0] @ np64(inp.k)[j, 0]) * c - first
+        say(f"  row {t} key {j}: score {jump:.1f} log2 units above its first tile's max")
+        assert jump > 20.0
+    # ramp: the last keys of every region are scaled up to 2.5x
+    ramp = torch.from_numpy(1.0 + 1.5 * (np.arange(inp.T) / inp.T) ** 2).to(torch.float32)
+    inp.k = (inp.k.float() * ramp[:, None, None]).to(torch.bfloat16)
+    say(f"case reference moves: P={P} lengths={lengths}")
+    got = run_gpu(inp)
+    ref = oracle_fwd_bwd(np64(inp.q), np64(inp.k), np64(inp.v), np64(inp.do), P, lengths, inp.scale)
+    check_all(got, ref, P, "reference moves")
+    rows = sorted({t for t, _, _ in plants})
+    e = rel(got["O"][rows], ref["O"][rows])
+    say(f"  planted rows O: rel {e:.2e}")
+    assert e <= REL
+    assert float(np.max(np.abs(got["LSE"][:, rows] - ref["LSE"][:, rows]))) <= LSE_ABS
 
 
 # ------------------------------------------------- several prompt groups --
@@ -343,15 +438,20 @@ def test_full_size_sampled(name):
                 say(f"  response {key} n={n} g={g}: rel {e:.2e}")
                 assert e <= REL, (key, n, g)
 
-    # 3. prompt keys against stored oracle values
+    # 3. prompt keys against stored oracle values (first and last KV head; first
+    #    and last keys of 16 key tiles, 32-key block edges, row-chunk edges)
     gpath = os.path.join(GOLDEN, f"prompt_keys_{name}.npz")
     gold = np.load(gpath)
     assert str(gold["digest"]) == inp.digest(), "inputs differ from the ones the goldens were made from"
-    keys, g = [int(x) for x in gold["keys"]], int(gold["kv_head"])
-    for key in ("dK", "dV"):
-        e = rel(got[key][keys, g], gold[key])
-        say(f"  prompt {key} (stored): rel {e:.2e}")
-        assert e <= REL, key
+    keys, heads = [int(x) for x in gold["keys"]], [int(x) for x in gold["kv_heads"]]
+    assert len(keys) >= 64 and heads == sorted({0, inp.Hkv - 1})
+    for i, g in enumerate(heads):
+        for key in ("dK", "dV"):
+            e = rel(got[key][keys, g], gold[key][i])
+            say(f"  prompt {key} kv_head={g} ({len(keys)} keys, stored): rel {e:.2e}")
+            assert e <= REL, (key, g)
+            worst = max(rel(got[key][j, g], gold[key][i, n]) for n, j in enumerate(keys))
+            say(f"    largest single-key rel error {worst:.2e}")
 
     # 4. sum rules: sum_j dK_j = 0 and sum_j dV_j = sum_{t, h in group} dO_t,h
     G = inp.Hq // inp.Hkv
@@ -361,6 +461,30 @@ def test_full_size_sampled(name):
         sv = got["dV"][:, g].astype(np.float64).sum(0)
         want = do[:, g * G:(g + 1) * G].astype(np.float64).sum((0, 1))
         assert rel(sv, want) <= REL, ("sum dV", g)
+
+
+def test_qwen3_heads_elementwise_first_and_last_kv_head():
+    """The Qwen3-8B-head workload (P = 4096, N = 8 responses of 4096, Q/K/V x0.5)
+    in full for KV heads 0 and 7 and their query heads: every element of O,
+    LSE and dQ of those query heads and of dK, dV of those KV heads against the
+    replicated oracle (heads are independent, so this is the literal check of
+    those heads at full sequence length)."""
+    name = "qwen3_8b_p4k_r4k_n8"
+    w = WORKLOADS[name]
+    inp = workload_inputs(w)
+    say(f"case {name}: T={inp.T} running fwd+bwd on the GPU")
+    got = run_gpu(inp)
+    G = inp.Hq // inp.Hkv
+    q, k, v, do = (np64(t) for t in (inp.q, inp.k, inp.v, inp.do))
+    for g in sorted({0, inp.Hkv - 1}):
+        say(f"case {name}: replicated oracle for kv head {g}")
+        ref = oracle_fwd_bwd(q, k, v, do, inp.P, inp.lengths, inp.scale, kv_heads=[g])
+        hs = slice(g * G, (g + 1) * G)
+        sub = {"O": got["O"][:, hs], "dQ": got["dQ"][:, hs], "dK": got["dK"][:, g], "dV": got["dV"][:, g],
+               "LSE": got["LSE"][hs]}
+        want = {"O": ref["O"][:, hs], "dQ": ref["dQ"][:, hs], "dK": ref["dK"][:, g], "dV": ref["dV"][:, g],
+                "LSE": ref["LSE"][hs]}
+        check_all(sub, want, inp.P, f"kv head {g}")
 
 
 def test_tensors_beyond_2_31_elements_sampled():
