@@ -23,7 +23,8 @@ EXPORTS = ("dualkv_fwd_workspace_bytes", "dualkv_bwd_workspace_bytes", "dualkv_f
            "dualkv_fwd_workspace_bytes_groups", "dualkv_bwd_workspace_bytes_groups",
            "dualkv_fwd_groups", "dualkv_bwd_groups",
            "dualkv_fwd_workspace_bytes_tree", "dualkv_bwd_workspace_bytes_tree",
-           "dualkv_fwd_tree", "dualkv_bwd_tree")
+           "dualkv_fwd_tree", "dualkv_bwd_tree", "dualkv_fwd_noalloc")
+NOALLOC_SCRATCH_BYTES = 128 << 20   # DUALKV_NOALLOC_SCRATCH_BYTES
 PHASE_PRE, PHASE_MAIN, PHASE_FINISH, PHASE_DQ, PHASE_ALL = 1, 2, 4, 8, 15
 
 _lib = None
@@ -76,6 +77,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dualkv_fwd_tree.argtypes = [vp, vp, vp, vp, vp] + targs + [c_float, vp, c_size, vp]
     lib.dualkv_bwd_tree.restype = c_int
     lib.dualkv_bwd_tree.argtypes = [vp] * 9 + targs + [c_float, c_int, vp, c_size, vp]
+    lib.dualkv_fwd_noalloc.restype = c_int
+    lib.dualkv_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, c_int, c_int, c_int, i32p, c_int, c_int,
+                                       c_int, c_float, vp]
     lib.dualkv_status_string.restype = ctypes.c_char_p
     lib.dualkv_status_string.argtypes = [c_int]
     _lib = lib
@@ -360,6 +364,27 @@ def bwd_tree(q, k, v, o, lse, do, tp: TreePacking, scale: Optional[float] = None
                                   float(scale), int(deterministic), _ptr(workspace),
                                   workspace.numel(), _stream_ptr(stream)))
     return dq, dk, dv
+
+
+def fwd_noalloc(q, k, v, pk: Packing, scale: Optional[float] = None, out=None, lse=None, stream=None):
+    """dualkv_fwd_noalloc -> (o, lse): the forward with the library's fixed
+    device scratch instead of a workspace (the library call allocates nothing;
+    o and lse are allocated here only if not given)."""
+    _, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    for name, t, hh in (("q", q, Hq), ("k", k, Hkv), ("v", v, Hkv)):
+        _check_tensor(name, t, (pk.T, hh, d), torch.bfloat16, dev)
+    scale = d ** -0.5 if scale is None else scale
+    with _alloc_on(stream):
+        out = torch.empty_like(q) if out is None else out
+        lse = torch.empty((Hq, pk.T), dtype=torch.float32, device=dev) if lse is None else lse
+    _check_tensor("o", out, (pk.T, Hq, d), torch.bfloat16, dev)
+    _check_tensor("lse", lse, (Hq, pk.T), torch.float32, dev)
+    _check(load().dualkv_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), pk.P, pk.R,
+                                     pk.N, pk.offsets_ptr(), Hq, Hkv, d, float(scale),
+                                     _stream_ptr(stream)))
+    return out, lse
 
 
 class DualKVAttention(torch.autograd.Function):

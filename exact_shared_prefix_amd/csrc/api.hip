@@ -441,6 +441,155 @@ dualkv_status bwd_impl(Problem& pb, const void* q, const void* k, const void* v,
   return DUALKV_OK;
 }
 
+// ------------------------------------------------ allocation-free forward --
+// dualkv_fwd_noalloc: the forward with its workspace in a fixed device array
+// of this library (one per GPU, held until the process ends) instead of a
+// caller buffer, and its work lists built on the device by describe_kernel
+// from the shape passed by value, so the call allocates nothing and copies
+// nothing from the host. Everything in the array is written before it is
+// read, so nothing needs clearing between calls; calls that overlap on one
+// GPU share the array and race.
+constexpr size_t kScratchBytes = DUALKV_NOALLOC_SCRATCH_BYTES;
+constexpr int kNoallocMaxResp = 256;     // responses per call (offsets travel by value)
+constexpr int kNoallocMaxItems = 4096;   // forward work items (256-row query tiles)
+constexpr int kNoallocMaxDevices = 16;
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+struct DescribeArgs {
+  int P, N;
+  int items_prompt, n_items;
+  int off[kNoallocMaxResp + 1];   // o_0 = P .. o_N = T
+};
+
+// Segment s of the single-group layout: s = 0 is the prompt [0, P), s = n + 1
+// is response n [o_n, o_{n+1}).
+__device__ inline int seg_begin(const DescribeArgs& a, int s) { return s == 0 ? 0 : a.off[s - 1]; }
+__device__ inline int seg_end(const DescribeArgs& a, int s) { return s == 0 ? a.P : a.off[s]; }
+
+// One workgroup writes the three lists fwd_items / key_blocks build on the
+// host, in the same order: the query tiles (kFwdRows rows of one segment) in
+// generation order get their key regions (the prompt tile [0, r1); a
+// response tile the whole prompt, then its own rows up to r1), and are then
+// placed by a stable rank on their key count, longest first.
+__global__ __launch_bounds__(1024) void describe_kernel(DescribeArgs a, FwdItem* __restrict__ items,
+                                                        Region* __restrict__ regions,
+                                                        KeyBlock* __restrict__ blocks) {
+  __shared__ int item_base[kNoallocMaxResp + 2];    // first item of segment s
+  __shared__ int block_base[kNoallocMaxResp + 2];   // first 32-key block of segment s
+  __shared__ int keys[kNoallocMaxItems];
+  const int nseg = a.N + 1;
+  if (threadIdx.x == 0) {
+    int it = 0, bl = 0;
+    for (int s = 0; s < nseg; ++s) {
+      item_base[s] = it;
+      block_base[s] = bl;
+      const int len = seg_end(a, s) - seg_begin(a, s);
+      it += (len + kFwdRows - 1) / kFwdRows;
+      bl += (len + 31) / 32;
+    }
+    item_base[nseg] = it;
+    block_base[nseg] = bl;
+  }
+  __syncthreads();
+  // items in generation order: key counts, regions
+  for (int i = threadIdx.x; i < a.n_items; i += blockDim.x) {
+    int s = 0;
+    while (item_base[s + 1] <= i) ++s;
+    const int b0 = seg_begin(a, s), b1 = seg_end(a, s);
+    const int r0 = b0 + (i - item_base[s]) * kFwdRows, r1 = min(b1, r0 + kFwdRows);
+    if (s == 0) {
+      keys[i] = r1;
+      regions[i] = Region{0, r1, block_base[0]};
+    } else {
+      keys[i] = a.P + (r1 - b0);
+      const int ro = a.items_prompt + 2 * (i - a.items_prompt);
+      regions[ro] = Region{0, a.P, block_base[0]};
+      regions[ro + 1] = Region{b0, r1, block_base[s]};
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < a.n_items; i += blockDim.x) {
+    int s = 0;
+    while (item_base[s + 1] <= i) ++s;
+    const int b0 = seg_begin(a, s), b1 = seg_end(a, s);
+    const int r0 = b0 + (i - item_base[s]) * kFwdRows, r1 = min(b1, r0 + kFwdRows);
+    const int ki = keys[i];
+    int rank = 0;
+    for (int j = 0; j < a.n_items; ++j) rank += (keys[j] > ki) || (keys[j] == ki && j < i);
+    items[rank] = s == 0 ? FwdItem{r0, r1, i, 1}
+                         : FwdItem{r0, r1, a.items_prompt + 2 * (i - a.items_prompt), 2};
+  }
+  for (int b = threadIdx.x; b < block_base[nseg]; b += blockDim.x) {
+    int s = 0;
+    while (block_base[s + 1] <= b) ++s;
+    blocks[b] = KeyBlock{seg_begin(a, s) + 32 * (b - block_base[s]), seg_end(a, s)};
+  }
+}
+
+// Device address of this GPU's scratch array, looked up once per device
+// with that device current (the array's name is only a host-side handle).
+hipError_t scratch_ptr(void** out) {
+  static std::mutex mu;
+  static void* ptr[kNoallocMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kNoallocMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return hipSuccess;
+}
+
+dualkv_status fwd_noalloc_impl(const Problem& pb, int P, const void* q, const void* k, const void* v,
+                               void* o, float* lse, float softmax_scale, void* stream) {
+  if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return DUALKV_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return DUALKV_ERR_INVALID_ARG;
+  const int N = (int)pb.segs.size() - 1;
+  if (N > kNoallocMaxResp) return DUALKV_ERR_UNSUPPORTED;
+  DescribeArgs a{};
+  a.P = P;
+  a.N = N;
+  long long n_blocks = 0;
+  for (int s = 0; s <= N; ++s) {
+    const Segment& sg = pb.segs[s];
+    if (s > 0) a.off[s - 1] = sg.start;
+    const int ni = (sg.len + kFwdRows - 1) / kFwdRows;
+    if (s == 0) a.items_prompt = ni;
+    a.n_items += ni;
+    n_blocks += (sg.len + 31) / 32;
+  }
+  a.off[N] = pb.T;
+  if (a.n_items > kNoallocMaxItems) return DUALKV_ERR_WORKSPACE;
+  const int n_regions = a.items_prompt + 2 * (a.n_items - a.items_prompt);
+  Problem sized = pb;
+  sized.scale = softmax_scale;
+  const FwdLayout L = fwd_layout(sized, a.n_items, n_regions, (size_t)n_blocks);
+  if (L.total > kScratchBytes) return DUALKV_ERR_WORKSPACE;
+  if (a.n_items == 0) return DUALKV_OK;
+  void* base = nullptr;
+  if (scratch_ptr(&base) != hipSuccess) return DUALKV_ERR_HIP;
+  char* ws = static_cast<char*>(base);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  FwdItem* items = reinterpret_cast<FwdItem*>(ws + L.items);
+  Region* regions = reinterpret_cast<Region*>(ws + L.regions);
+  KeyBlock* blocks = reinterpret_cast<KeyBlock*>(ws + L.blocks);
+  hipLaunchKernelGGL(describe_kernel, dim3(1), dim3(1024), 0, s, a, items, regions, blocks);
+  if (hipGetLastError() != hipSuccess) return DUALKV_ERR_HIP;
+  const int max_regions = a.n_items > a.items_prompt ? 2 : 1;
+  if (launch_xpose_kv(sized, v, ws + L.vt, blocks, (int)n_blocks, s) != hipSuccess ||
+      launch_fwd(sized, q, k, ws + L.vt, o, lse, items, regions, a.n_items, max_regions, s) != hipSuccess)
+    return DUALKV_ERR_HIP;
+  return DUALKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -575,6 +724,15 @@ dualkv_status dualkv_bwd_tree(const void* q, const void* k, const void* v, const
   if (st != DUALKV_OK) return st;
   return bwd_impl(pb, q, k, v, o, lse, dO, dQ, dK, dV, softmax_scale, deterministic, workspace,
                   workspace_bytes, stream, 15);
+}
+
+dualkv_status dualkv_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int P, int R, int N, const int32_t* offsets, int Hq, int Hkv,
+                                 int d, float softmax_scale, void* stream) {
+  Problem pb;
+  const dualkv_status st = check_shape(P, R, N, offsets, Hq, Hkv, d, pb);
+  if (st != DUALKV_OK) return st;
+  return fwd_noalloc_impl(pb, P, q, k, v, o, lse, softmax_scale, stream);
 }
 
 }  // extern "C"

@@ -188,6 +188,28 @@ dualkv_status dualkv_bwd_tree(const void* q, const void* k, const void* v, const
                               int Hq, int Hkv, int d, float softmax_scale, int deterministic,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory or stage host copies (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): dualkv_fwd with no workspace argument. Same arguments, layouts,
+ * checks and results as dualkv_fwd (bitwise: the kernels are the same); the
+ * work lists and the V^T fragments live in a fixed device array inside the
+ * library, DUALKV_NOALLOC_SCRATCH_BYTES per GPU, reserved when the library's
+ * code is loaded on that GPU and held until the process ends. The work lists
+ * are built on the device from the shape passed by value, so the call makes no
+ * allocation of any kind, no host-to-device copy and no synchronisation: it
+ * enqueues three kernels on `stream`. Limits: at most 256 responses
+ * (DUALKV_ERR_UNSUPPORTED beyond), at most 4096 query tiles of 256 rows, and
+ * work lists plus V^T (about 2 * T * Hkv * d bytes) within the array
+ * (DUALKV_ERR_WORKSPACE beyond); these checks come before any HIP call.
+ * Every call on one GPU uses that GPU's array, and everything a call reads
+ * there it has written first, so nothing carries over from the previous
+ * call; but calls that overlap in time on one GPU (other streams, other
+ * threads) race on it and must be ordered by the caller. */
+#define DUALKV_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+dualkv_status dualkv_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int P, int R, int N, const int32_t* offsets,
+                                 int Hq, int Hkv, int d, float softmax_scale, void* stream);
+
 /* Static English description of a status code (never NULL). */
 const char* dualkv_status_string(dualkv_status s);
 

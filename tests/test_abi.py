@@ -230,3 +230,31 @@ def test_pair_accounting_matches_brute_force():
         assert metrics.pairs(P, lengths) == brute
         rep = sum(sum(range(1, P + r + 1)) for r in lengths)
         assert metrics.replicated_pairs(P, lengths) == rep
+
+
+def _fwd_noalloc(lib, P=16, R=8, N=2, offsets=None, Hq=4, Hkv=2, d=128, scale=0.1, q=FAKE):
+    offp = None
+    if offsets is not None:
+        arr = (ctypes.c_int32 * len(offsets))(*offsets)
+        offp = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+    return lib.dualkv_fwd_noalloc(q, FAKE, FAKE, FAKE, FAKE, P, R, N, offp, Hq, Hkv, d, scale, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=0), ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=4), ERR_INVALID_ARG),
+    (dict(d=96), ERR_UNSUPPORTED),
+    (dict(scale=-1.0), ERR_INVALID_ARG),
+    (dict(q=FAKE + 2), ERR_INVALID_ARG),
+    (dict(N=257, R=4), ERR_UNSUPPORTED),                      # more responses than travel by value
+    (dict(P=1 << 20, Hkv=8, Hq=8, d=128), ERR_WORKSPACE),     # V^T alone is 2 GiB > the fixed array
+    (dict(P=1 << 16, R=0, N=1, Hkv=8, Hq=8, d=128), ERR_WORKSPACE),   # 256 tiles fit, V^T (128 MiB) does not
+])
+def test_fwd_noalloc_rejects_what_exceeds_its_scratch(lib, kw, status):
+    assert _fwd_noalloc(lib, **kw) == status
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define DUALKV_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == binding.NOALLOC_SCRATCH_BYTES
