@@ -79,8 +79,11 @@ def replicated_inputs(q, k, v, do, P, lengths):
             do.index_select(0, idx), [P + r for r in lengths])
 
 
-def time_steps(q, k, v, do, pk, scale, steps, warmup, phase_events=True, deterministic=False):
-    """Run warmup + timed fwd+bwd steps; returns timings in ms."""
+def time_steps(q, k, v, do, pk, scale, steps, warmup, phase_events=True, deterministic=False,
+               queued=False):
+    """Run warmup + timed fwd+bwd steps; returns timings in ms. queued: hold
+    the GPU in a spin kernel while the host enqueues all timed steps, so the
+    timed region is the GPU's own execution with no wait for the host."""
     import torch
     from exact_shared_prefix_amd import binding
     dev = q.device
@@ -116,6 +119,8 @@ def time_steps(q, k, v, do, pk, scale, steps, warmup, phase_events=True, determi
     t_all1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
+    if queued:
+        torch.cuda._sleep(int(2e8))   # ~0.1 s of spinning: longer than enqueueing the steps
     t_all0.record(stream)
     for i in range(steps):
         step(evs[i] if phase_events else None)
@@ -207,9 +212,9 @@ def calibrate_copy(nbytes: int) -> None:
 def group_main(args, name: str) -> int:
     """Several prompt groups per call (dualkv_fwd_groups / dualkv_bwd_groups):
     the same JSON line for a multi-group workload. The group entry points have
-    no per-phase split, so the roofline is taken over the whole fwd+bwd step
-    with the algorithmic FLOPs of all three kernels (4 d + 8 d + 6 d per pair
-    and query head)."""
+    no per-phase split, so the roofline is taken over the whole fwd+bwd step on
+    its useful FLOPs (14 d per pair and query head), with the executed ones
+    (18 d: the dQ pass recomputes S and dP) beside them."""
     import torch
 
     from exact_shared_prefix_amd import binding, metrics
@@ -297,10 +302,11 @@ def group_main(args, name: str) -> int:
                    "useful_tflop_per_step": useful / 1e12, "parallelism": "single GPU"},
         "timing_ms": {kk: round(vv, 4) for kk, vv in t.items()},
         "roofline": {"bound": "mfma", "kernel": "fwd+bwd step (all kernels)",
-                     "achieved": executed / (ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": executed / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "traffic": None,
+                     "achieved": useful / (ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": useful / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "traffic": None,
                      "traffic_source": "no counters for this workload",
-                     "algorithmic_flop_per_step": executed},
+                     "algorithmic_flop_per_step": useful, "executed_flop_per_step": executed,
+                     "executed_tflops": executed / (ms * 1e-3) / 1e12},
         "peak_hbm_gb": peak / 1e9, "replicated": rep, "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
@@ -333,7 +339,9 @@ def sweep_main(args) -> int:
     kernels on the replicated layout, the token compression
     rho = N(P+R)/(P+NR) and the pair ratio, one JSON line per point and a
     Markdown table on stderr. Where the packed layout stops paying off is
-    the row where the speed-up approaches 1."""
+    the row where the speed-up approaches 1. Each packed point is also timed
+    with its launches queued behind a spin kernel: the gap between the two
+    times is the host's share (argument checks, work lists, launches)."""
     import torch
 
     from exact_shared_prefix_amd import binding, metrics
@@ -344,13 +352,14 @@ def sweep_main(args) -> int:
     Hq, Hkv, d = 32, 8, 128
     rows = []
     steps, warmup = max(2, args.steps // 3), 1
-    for P in SWEEP_P:
+    for P in (args.sweep_p or SWEEP_P):
         for R in SWEEP_R:
             for N in SWEEP_N:
                 L = [R] * N
                 inp = make_inputs(P, L, Hq, Hkv, d, seed=7)
                 q, k, v, do = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.do))
                 t = time_steps(q, k, v, do, binding.Packing(P, L), inp.scale, steps, warmup, False)
+                tq = time_steps(q, k, v, do, binding.Packing(P, L), inp.scale, steps, 0, False, queued=True)
                 rq, rk, rv, rd, rlen = replicated_inputs(q, k, v, do, P, L)
                 del q, k, v, do
                 rt = time_steps(rq, rk, rv, rd, binding.Packing(0, rlen), inp.scale, steps, warmup, False)
@@ -358,7 +367,9 @@ def sweep_main(args) -> int:
                 torch.cuda.empty_cache()
                 packed_tok, rep_tok = metrics.tokens(P, L)
                 pairs = metrics.pairs(P, L)
-                rec = {"P": P, "R": R, "N": N, "packed_ms": t["ms_per_step"], "replicated_ms": rt["ms_per_step"],
+                rec = {"P": P, "R": R, "N": N, "packed_ms": t["ms_per_step"],
+                       "packed_gpu_ms": tq["ms_per_step"], "host_share": 1 - tq["ms_per_step"] / t["ms_per_step"],
+                       "replicated_ms": rt["ms_per_step"],
                        "speedup": rt["ms_per_step"] / t["ms_per_step"], "rho_tokens": rep_tok / packed_tok,
                        "pair_ratio": metrics.replicated_pairs(P, L) / pairs,
                        "useful_tflops": 14 * d * Hq * pairs / (t["ms_per_step"] * 1e-3) / 1e12}
@@ -366,11 +377,13 @@ def sweep_main(args) -> int:
                 print(json.dumps(rec), flush=True)
                 log(f"[sweep] P={P} R={R} N={N}: packed {t['ms_per_step']:.2f} ms, replicated "
                     f"{rt['ms_per_step']:.2f} ms, speed-up {rec['speedup']:.2f}x (pairs ratio {rec['pair_ratio']:.2f})")
-    log("| P | R | N | packed ms | replicated ms | speed-up | pair ratio | token ratio rho | useful TFLOP/s |")
-    log("|---|---|---|---|---|---|---|---|---|")
+    log("| P | R | N | packed ms | packed ms, launches queued | replicated ms | speed-up | pair ratio | "
+        "token ratio rho | useful TFLOP/s |")
+    log("|---|---|---|---|---|---|---|---|---|---|")
     for r in rows:
-        log(f"| {r['P']} | {r['R']} | {r['N']} | {r['packed_ms']:.2f} | {r['replicated_ms']:.2f} | "
-            f"{r['speedup']:.2f} | {r['pair_ratio']:.2f} | {r['rho_tokens']:.2f} | {r['useful_tflops']:.0f} |")
+        log(f"| {r['P']} | {r['R']} | {r['N']} | {r['packed_ms']:.2f} | {r['packed_gpu_ms']:.2f} | "
+            f"{r['replicated_ms']:.2f} | {r['speedup']:.2f} | {r['pair_ratio']:.2f} | {r['rho_tokens']:.2f} | "
+            f"{r['useful_tflops']:.0f} |")
     return 0
 
 
@@ -484,7 +497,11 @@ def tree_main(args) -> int:
     rp = binding.Packing(0, [S + P + R] * (B * N))
     ms_r, mem_r = timed(rp.T, lambda q, k, v: binding.fwd(q, k, v, rp),
                         lambda q, k, v, o, lse, do: binding.bwd(q, k, v, o, lse, do, rp))
+    from exact_shared_prefix_amd import metrics
+    useful = 14 * d * Hq * metrics.tree_pairs(node_len, node_parent)
     rec = {"metric": "two-level shared prefix: fwd+bwd ms, tree vs flat groups vs replicated",
+           "useful_tflops": useful / (ms_t * 1e-3) / 1e12,
+           "frac_of_peak": useful / (ms_t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
            "config": {"system_prompt": S, "groups": B, "P": P, "N": N, "R": R, "Hq": Hq, "Hkv": Hkv,
                       "head_dim": d},
            "tree": {"tokens": tp.T, "ms": ms_t, "peak_hbm_gb": mem_t / 1e9},
@@ -515,6 +532,8 @@ def main() -> int:
                     help="two-level shared prefix (system prompt + prompt groups) vs flat groups")
     ap.add_argument("--sweep", action="store_true",
                     help="N/P/R sweep of packed vs replicated time (one JSON line per point)")
+    ap.add_argument("--sweep-p", type=int, nargs="*", default=None, metavar="P",
+                    help="restrict the sweep to these prompt lengths")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -569,21 +588,25 @@ def main() -> int:
         f"dQ {packed['bwd_dq_ms']:.2f} ms)")
 
     kflops = metrics.kernel_flops(P, L, inp.Hq, inp.d)
-    kernels = {
-        "fwd_kernel": {"ms": packed["fwd_ms"], "flops": kflops["fwd_kernel"]},
-        "dkv_kernel": {"ms": packed["bwd_dkv_ms"], "flops": kflops["dkv_kernel"]},
-        "dq_kernel": {"ms": packed["bwd_dq_ms"], "flops": kflops["dq_kernel"]},
-    }
-    dom = max(kernels, key=lambda n: kernels[n]["ms"])
-    ach = kernels[dom]["flops"] / (kernels[dom]["ms"] * 1e-3) / 1e12
+    kuseful = metrics.kernel_useful_flops(P, L, inp.Hq, inp.d)
+    kms = {"fwd_kernel": packed["fwd_ms"], "dkv_kernel": packed["bwd_dkv_ms"],
+           "dq_kernel": packed["bwd_dq_ms"]}
+    dom = max(kms, key=lambda n: kms[n])
+    # the dominant kernel's work is all useful (the backward's S, dP, dV, dK)
+    ach = kuseful[dom] / (kms[dom] * 1e-3) / 1e12
     traffic, traffic_src = stored_traffic(dom, name)
     roofline = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": traffic,
                 "traffic_source": traffic_src,
-                "algorithmic_flop_per_launch": kernels[dom]["flops"],
-                "avg_launch_ms": kernels[dom]["ms"]}
-    other = {n: {"ms": kv["ms"], "tflops": kv["flops"] / (kv["ms"] * 1e-3) / 1e12}
-             for n, kv in kernels.items()}
+                "algorithmic_flop_per_launch": kuseful[dom],
+                "executed_flop_per_launch": kflops[dom],
+                "avg_launch_ms": kms[dom]}
+    # per kernel: the useful part of its work and everything it executes
+    # (they differ only for the dQ pass, which recomputes S and dP)
+    other = {n: {"ms": kms[n], "useful_tflop": kuseful[n] / 1e12, "executed_tflop": kflops[n] / 1e12,
+                 "useful_tflops": kuseful[n] / (kms[n] * 1e-3) / 1e12,
+                 "executed_tflops": kflops[n] / (kms[n] * 1e-3) / 1e12}
+             for n in kms}
 
     deterministic = None
     if not args.no_deterministic:

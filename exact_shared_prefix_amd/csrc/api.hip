@@ -33,7 +33,14 @@ using namespace dkv;
 
 namespace {
 
-constexpr int kBwdChunk = 2048; // query rows per dK/dV work item (grid of row chunks)
+// Query rows per dK/dV work item (the grid of row chunks): the largest of
+// 2048, 1024, 512, 256 that gives the dK/dV pass at least kBwdMinGroups
+// workgroups (one per CU), else the one that gives it the most. Shorter
+// chunks mean more partial dK/dV flushes, so they are taken only where the
+// pass would otherwise leave CUs idle.
+constexpr int kBwdChunk = 2048;
+constexpr int kMinBwdChunk = 256;
+constexpr long long kBwdMinGroups = 256;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -260,10 +267,32 @@ std::vector<FwdItem> fwd_items(const Problem& pb, std::vector<Region>* regions, 
   return items;
 }
 
+// dK/dV items of a chunk size C: every key tile paired with each C-row chunk
+// its attending rows (from the tile's first key to the end of its segment's
+// subtree) touch.
+long long bwd_item_count(const Problem& pb, int C) {
+  long long n = 0;
+  for (const Segment& sg : pb.segs)
+    for (int kb = sg.start; kb < sg.start + sg.len; kb += kBwdKeys)
+      if (kb < sg.subtree_end) n += (sg.subtree_end - 1) / C - kb / C + 1;
+  return n;
+}
+
+int chunk_rows(const Problem& pb) {
+  int best = kBwdChunk;
+  long long most = 0;
+  for (int C = kBwdChunk; C >= kMinBwdChunk; C /= 2) {
+    const long long n = bwd_item_count(pb, C);
+    if (n * pb.Hkv >= kBwdMinGroups) return C;
+    if (n > most) { most = n; best = C; }
+  }
+  return best;
+}
+
 // dK/dV work list: kBwdKeys-key tiles of each segment, each paired with the
 // rows that attend it: the later rows of the segment's subtree (every later row
 // of its group for a prompt tile, the later rows of its own response for a
-// response tile), cut on a fixed grid of kBwdChunk-row chunks.
+// response tile), cut on a fixed grid of chunk_rows(pb)-row chunks.
 // Items are ordered chunk-major so workgroups running together share query
 // rows. With tl_out != null, also returns each tile's items (ascending) as a
 // CSR list.
@@ -277,9 +306,10 @@ std::vector<BwdItem> bwd_items(const Problem& pb, TileLists* tl_out = nullptr) {
   }
   std::vector<BwdItem> items;
   std::vector<std::vector<int>> per_tile(tiles.size());
-  const int nchunks = (pb.T + kBwdChunk - 1) / kBwdChunk;
+  const int chunk = chunk_rows(pb);
+  const int nchunks = (pb.T + chunk - 1) / chunk;
   for (int cidx = 0; cidx < nchunks; ++cidx) {
-    const int c0 = cidx * kBwdChunk, c1 = std::min(pb.T, c0 + kBwdChunk);
+    const int c0 = cidx * chunk, c1 = std::min(pb.T, c0 + chunk);
     for (size_t ti = 0; ti < tiles.size(); ++ti) {
       const Tile& tl = tiles[ti];
       const int r0 = std::max(c0, tl.kb), r1 = std::min(c1, tl.rend);
@@ -348,14 +378,32 @@ size_t fwd_ws_bytes(const Problem& pb) {
   return fwd_layout(pb, ni, regs.size(), key_blocks(pb).size()).total;
 }
 
-size_t bwd_ws_bytes(const Problem& pb, bool det) {
-  TileLists tl;
-  const size_t ni = bwd_items(pb, &tl).size();
-  std::vector<Region> qregs;
-  const size_t nq = fwd_items(pb, &qregs, kDqRows).size();
-  return bwd_layout(pb, std::max<size_t>(1, ni), std::max<size_t>(1, nq), qregs.size(), det,
-                    tl.off.size() - 1).total;
+// Sizes of the backward's lists, counted without building them: dK/dV items
+// (key tiles x the row chunks their attending rows touch), key tiles, dQ
+// items (query tiles) and their key regions (ancestors + own segment each).
+struct BwdCounts { size_t items = 0, tiles = 0, qitems = 0, qregions = 0; };
+BwdCounts bwd_counts(const Problem& pb) {
+  BwdCounts n;
+  std::vector<int> depth(pb.segs.size(), 0);
+  for (size_t v = 0; v < pb.segs.size(); ++v) {
+    const Segment& sg = pb.segs[v];
+    if (sg.parent >= 0) depth[v] = depth[sg.parent] + 1;
+    const int e = sg.start + sg.len;
+    for (int kb = sg.start; kb < e; kb += kBwdKeys) ++n.tiles;
+    const size_t q = (size_t)(sg.len + kDqRows - 1) / kDqRows;
+    n.qitems += q;
+    n.qregions += q * (depth[v] + 1);
+  }
+  n.items = (size_t)bwd_item_count(pb, chunk_rows(pb));
+  return n;
 }
+
+BwdLayout bwd_layout_of(const Problem& pb, const BwdCounts& n, bool det) {
+  return bwd_layout(pb, std::max<size_t>(1, n.items), std::max<size_t>(1, n.qitems), n.qregions, det,
+                    n.tiles);
+}
+
+size_t bwd_ws_bytes(const Problem& pb, bool det) { return bwd_layout_of(pb, bwd_counts(pb), det).total; }
 
 dualkv_status fwd_impl(Problem& pb, const void* q, const void* k, const void* v, void* o,
                        float* lse, float softmax_scale, void* workspace, size_t workspace_bytes,
@@ -400,33 +448,41 @@ dualkv_status bwd_impl(Problem& pb, const void* q, const void* k, const void* v,
     return DUALKV_ERR_INVALID_ARG;
   pb.scale = softmax_scale;
   const bool det = deterministic != 0;
-  TileLists tl;
-  const std::vector<BwdItem> items = bwd_items(pb, &tl);
-  std::vector<Region> qregs;
-  const std::vector<FwdItem> qitems = fwd_items(pb, &qregs, kDqRows);
-  const int n_tiles = (int)tl.off.size() - 1;
-  const BwdLayout L = bwd_layout(pb, std::max<size_t>(1, items.size()),
-                                 std::max<size_t>(1, qitems.size()), qregs.size(), det, n_tiles);
+  const BwdCounts cnt = bwd_counts(pb);
+  const BwdLayout L = bwd_layout_of(pb, cnt, det);
   if (!workspace || workspace_bytes < L.total) return DUALKV_ERR_WORKSPACE;
   if (!aligned16(workspace)) return DUALKV_ERR_INVALID_ARG;
   if (pb.T == 0) return DUALKV_OK;
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // the dK/dV pass reads the item list, and so does the ordered reduction
+  // build and upload only what the requested phases read: the dK/dV pass and
+  // the ordered reduction read the item list, the reduction also the tile
+  // lists, the dQ pass its query-tile list and key regions
   const bool need_items = (phase_mask & 2) || (det && (phase_mask & 4));
+  const bool need_tiles = det && (phase_mask & 4);
+  const bool need_q = (phase_mask & 8) != 0;
+  TileLists tl;
+  std::vector<BwdItem> items;
+  if (need_items) items = bwd_items(pb, need_tiles ? &tl : nullptr);
+  std::vector<Region> qregs;
+  std::vector<FwdItem> qitems;
+  if (need_q) qitems = fwd_items(pb, &qregs, kDqRows);
+  if (items.size() > cnt.items || qitems.size() > cnt.qitems || qregs.size() > cnt.qregions)
+    return DUALKV_ERR_HIP;   // the counts size the workspace; they cannot fall short
   if (need_items && !items.empty() &&
       upload(ws + L.items, items.data(), items.size() * sizeof(BwdItem), s) != hipSuccess)
     return DUALKV_ERR_HIP;
-  if (det && (phase_mask & 4) && !items.empty() &&
+  if (need_tiles && !items.empty() &&
       (upload(ws + L.tile_off, tl.off.data(), tl.off.size() * sizeof(int), s) != hipSuccess ||
        upload(ws + L.tile_items, tl.items.data(), tl.items.size() * sizeof(int), s) != hipSuccess))
     return DUALKV_ERR_HIP;
-  if ((phase_mask & 8) && !qitems.empty() &&
+  if (need_q && !qitems.empty() &&
       (upload(ws + L.qitems, qitems.data(), qitems.size() * sizeof(FwdItem), s) != hipSuccess ||
        upload(ws + L.qregions, qregs.data(), qregs.size() * sizeof(Region), s) != hipSuccess))
     return DUALKV_ERR_HIP;
   int max_qregions = 1;
   for (const FwdItem& it : qitems) max_qregions = std::max(max_qregions, it.n_reg);
+  const int n_tiles = (int)cnt.tiles;
   if (launch_bwd(pb, q, k, v, o, lse, dO, dQ, dK, dV, reinterpret_cast<const BwdItem*>(ws + L.items),
                  (int)items.size(), reinterpret_cast<const FwdItem*>(ws + L.qitems),
                  reinterpret_cast<const Region*>(ws + L.qregions), (int)qitems.size(), max_qregions,

@@ -26,6 +26,20 @@ def pairs(P: int, lengths: Sequence[int]) -> int:
     return pair_blocks(P, lengths)["total"]
 
 
+def tree_pairs(node_len: Sequence[int], node_parent: Sequence[int]) -> int:
+    """Attended pairs per query head of a prefix forest (segments in
+    depth-first order): a row at offset i of segment v sees every key of v's
+    ancestors and keys 0 .. i of v."""
+    depth_keys = []
+    total = 0
+    for ln, par in zip(node_len, node_parent):
+        anc = 0 if par < 0 else depth_keys[par] + int(node_len[par])
+        depth_keys.append(anc)
+        ln = int(ln)
+        total += ln * anc + ln * (ln + 1) // 2
+    return total
+
+
 def replicated_pairs(P: int, lengths: Sequence[int]) -> int:
     """Pairs of the same batch with the prompt copied into every sequence."""
     return sum((P + int(r)) * (P + int(r) + 1) // 2 for r in lengths)
@@ -37,11 +51,20 @@ def useful_flops(P: int, lengths: Sequence[int], Hq: int, d: int) -> dict:
 
 
 def kernel_flops(P: int, lengths: Sequence[int], Hq: int, d: int) -> dict:
-    """Algorithmic FLOPs each kernel executes on attended pairs: the forward
-    (S, PV), the key-stationary dK/dV pass (S, dP, dV, dK) and the
-    query-stationary dQ pass (S, dP recomputed, dQ)."""
+    """FLOPs each kernel executes on attended pairs: the forward (S, PV), the
+    key-stationary dK/dV pass (S, dP, dV, dK) and the query-stationary dQ pass
+    (S and dP recomputed, dQ)."""
     n = pairs(P, lengths)
     return {"fwd_kernel": 4 * d * Hq * n, "dkv_kernel": 8 * d * Hq * n, "dq_kernel": 6 * d * Hq * n}
+
+
+def kernel_useful_flops(P: int, lengths: Sequence[int], Hq: int, d: int) -> dict:
+    """The part of each kernel's work that counts toward the useful 14 d per
+    pair: all of the forward (4 d) and of the dK/dV pass (8 d: the backward's
+    S, dP, dV, dK products), and only the dQ product (2 d) of the dQ pass, whose
+    S and dP are the dK/dV pass's products computed a second time."""
+    n = pairs(P, lengths)
+    return {"fwd_kernel": 4 * d * Hq * n, "dkv_kernel": 8 * d * Hq * n, "dq_kernel": 2 * d * Hq * n}
 
 
 def tokens(P: int, lengths: Sequence[int]) -> tuple[int, int]:

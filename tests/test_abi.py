@@ -232,6 +232,14 @@ def test_pair_accounting_matches_brute_force():
         assert metrics.replicated_pairs(P, lengths) == rep
 
 
+def test_tree_pair_accounting_matches_brute_force():
+    from oracle import attended_keys_tree
+    for node_len, node_parent in (([7, 3, 0, 5, 4, 2], [-1, 0, 1, 1, 0, -1]), ([4, 2, 3, 1], [-1, 0, 1, 2]),
+                                  ([5, 2, 0, 3], [-1, 0, 0, 0])):
+        brute = sum(len(attended_keys_tree(t, node_len, node_parent)) for t in range(sum(node_len)))
+        assert metrics.tree_pairs(node_len, node_parent) == brute
+
+
 def _fwd_noalloc(lib, P=16, R=8, N=2, offsets=None, Hq=4, Hkv=2, d=128, scale=0.1, q=FAKE):
     offp = None
     if offsets is not None:

@@ -189,11 +189,12 @@ def test_deterministic_mode_bitwise_repeat_multi_chunk():
 
 
 # ------------------------------------------------ across the row-chunk grid --
-# The dK/dV pass cuts every key tile's attending rows into 2048-row chunks; a
-# prompt key tile's gradient is the sum of the partials of all its chunks (fp32
-# atomics, or the ordered sum of the deterministic mode). These cases have
-# T > 4096, so prompt tiles span three or more chunks, and every element is
-# compared with the replicated oracle in both modes.
+# The dK/dV pass cuts every key tile's attending rows into row chunks (2048
+# rows; 256 to 1024 for problems too small to fill the chip with 2048-row
+# chunks, as these); a prompt key tile's gradient is the sum of the partials of
+# all its chunks (fp32 atomics, or the ordered sum of the deterministic mode).
+# These cases have T > 4096, so prompt tiles span many chunks, and every
+# element is compared with the replicated oracle in both modes.
 CHUNKED = {
     "chunks_p4096_gqa4_d128": dict(P=4096, lengths=[2500, 3000, 1800], Hq=8, Hkv=2, d=128, seed=34),
     "chunks_p2400_ragged_d64": dict(P=2400, lengths=[1900, 1500, 700, 3], Hq=2, Hkv=1, d=64, seed=37),
