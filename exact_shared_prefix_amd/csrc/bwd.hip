@@ -5,7 +5,7 @@
 // backward walks the same two disjoint KV regions as the forward, and the
 // shared prompt's key/value gradients are accumulated over all N sequences
 // with fp32 atomics. Here:
-//  1. pre_kernel:  D_t = sum_d dO_t * O_t (fp32), stored beside -LSE_t log2 e;
+//  1. pre_kernel:  D_t = sum_d dO_t * O_t (fp32), stored negated beside -LSE_t log2 e;
 //                  zero_kernel clears the fp32 dK, dV accumulators.
 //  2. dkv_kernel:  key-stationary dK, dV. A workgroup owns 256 keys of one KV
 //                  head (8 waves x 32 keys) and walks the query rows that
@@ -30,8 +30,9 @@ namespace dkv {
 
 // ------------------------------------------------------------------ pre --
 // One 16-lane group per (row, head): 16 lanes x 8 elements = 128 (d=64: 8 lanes).
-// Writes rs[h][t] = {-LSE_t log2 e, D_t}: the two per-row values both passes
-// read, the LSE already in the base-2 form the exponentials use.
+// Writes rs[h][t] = {-LSE_t log2 e, -D_t}: the two per-row values both passes
+// read, the LSE already in the base-2 form the exponentials use and D negated,
+// the value the dP products' accumulators start from (they end as dP - D).
 template <int D>
 __global__ __launch_bounds__(256) void pre_kernel(const u16* __restrict__ o,
                                                   const u16* __restrict__ dO,
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(256) void pre_kernel(const u16* __restrict__ o,
   if (valid && sub == 0) {
     const int t = (int)(rh / Hq), h = (int)(rh % Hq);
     const size_t i = (size_t)h * T + t;
-    rs[i] = make_float2(-lse[i] * kLog2e, acc);
+    rs[i] = make_float2(-lse[i] * kLog2e, -acc);
   }
 }
 
@@ -118,6 +119,7 @@ __device__ __forceinline__ void store_dkv(const f32x16* dkacc, const f32x16* dva
 // qb.., head h):
 //   S = Q K^T, P = exp2(S c - LSE log2 e), dP = dO V^T, dS = P (dP - D),
 //   dV += P^T dO, dK += dS^T Q.
+// The dP accumulator starts at -D rather than zero, so dS is one product.
 // S and dP are computed with queries as rows, so a lane owns one key and the
 // P / dS accumulators are directly the A operands of the dV / dK products.
 // Q and dO arrive by direct copies one step ahead. For d = 128 they are
@@ -147,7 +149,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
   u16* const QA1 = smem + TS;
   u16* const OA0 = smem + 2 * TS;
   u16* const OA1 = smem + 3 * TS;
-  float* const LD0 = reinterpret_cast<float*>(smem + 4 * TS);   // per wave: -LSE log2 e (32) | D (32)
+  float* const LD0 = reinterpret_cast<float*>(smem + 4 * TS);   // per wave: -LSE log2 e (32) | -D (32)
   float* const LD1 = LD0 + NW * 64;
   u16* const KF = reinterpret_cast<u16*>(LD1 + NW * 64);          // K B fragments per wave
   // Q^T, dO^T B fragments [dt][ks] (d = 64 only)
@@ -233,7 +235,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
         else dma16(op + 16 * (f - NKK), oa + (f - NKK) * kFrag);
       }
     }
-    // lane l < 32: -LSE log2 e of row qb + l; lane 32 + l: D of that row
+    // lane l < 32: -LSE log2 e of row qb + l; lane 32 + l: -D of that row
     dma4s(rs + (size_t)h * T + qb, 4u * (2u * (uint32_t)min(l32, lim) + (uint32_t)hl), ld + 64 * w);
   };
   const uint32_t abase = row_a_base(lane), bbase = row_b_base(lane);
@@ -260,6 +262,19 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
     bf16x8 pf[2], sf[2];
     const bool active = kw < it.ke && kw <= qb + BQ - 1;
     if (active) {
+      // -D of the step's rows (read before the S products, which hide its latency)
+      f32x16 ndacc;
+      {
+        const float* lw = ld + 64 * w;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 d4 = *reinterpret_cast<const float4*>(lw + 32 + 8 * g4 + 4 * hl);
+          ndacc[4 * g4 + 0] = d4.x;
+          ndacc[4 * g4 + 1] = d4.y;
+          ndacc[4 * g4 + 2] = d4.z;
+          ndacc[4 * g4 + 3] = d4.w;
+        }
+      }
       f32x16 sacc = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk)
@@ -290,22 +305,14 @@ __global__ __launch_bounds__(64 * kBwdWaves, 1) void dkv_kernel(
       }
       pack2(sacc, pf[0], pf[1]);
 
-      f32x16 dpacc = f32x16{};
+      f32x16 dpacc = ndacc;   // starts at -D, ends as dP - D
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk)
         dpacc = mfma32(kRow ? row_ld_a(oa, abase ^ (32 * kk)) : frag_ld(oa + kk * kFrag, lane), vf[kk], dpacc);
       pipelined_mfma<NKK, 1, 4>();
       if (st + 1 < nsteps) stage(nq, g * G + nh, qan, oan, ldn);
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const float4 d4 = *reinterpret_cast<const float4*>(lw + 32 + 8 * g4 + 4 * hl);
-        const float da[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g4 + e;
-          dpacc[r] = sacc[r] * (dpacc[r] - da[e]);   // dS from the fp32 P
-        }
-      }
+      for (int r = 0; r < 16; ++r) dpacc[r] = sacc[r] * dpacc[r];   // dS from the fp32 P
       pack2(dpacc, sf[0], sf[1]);
       // dS complete before the dV, dK products: with its registers free the
       // B-fragment reads of those products are issued an MFMA ahead (mixed
@@ -474,11 +481,14 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
     }
   }
   const float2 rst = rs[(size_t)h * T + tc];
-  const float nlse2 = rst.x, dl = rst.y;   // -LSE log2 e, D
+  const float nlse2 = rst.x, ndv = rst.y;   // -LSE log2 e, -D
   // complete these loads before the tile loop (see the forward-copy waits)
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) asm volatile("" ::"v"(qf[kk]), "v"(of[kk]));
-  asm volatile("" ::"v"(nlse2), "v"(dl));
+  asm volatile("" ::"v"(nlse2), "v"(ndv));
+  f32x16 ndl;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ndl[r] = ndv;
 
   f32x16 dqacc[NDT];
 #pragma unroll
@@ -572,7 +582,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
       pipelined_mfma<NKK, 1, 4>();
       // dP^T does not depend on P: its products go first, so the exponentials
       // below overlap the end of the chain
-      f32x16 dpacc = f32x16{};
+      f32x16 dpacc = ndl;   // starts at -D, ends as dP^T - D
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) dpacc = mfma32(frag_ld(va + (kb2 * NKK + kk) * kFrag, lane), of[kk], dpacc);
       pipelined_mfma<NKK, 1, 4>();
@@ -589,7 +599,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(
         for (int r = 0; r < 16; ++r) sacc[r] = fast_exp2(fmaf(sacc[r], c, nlse2));
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dpacc[r] = sacc[r] * (dpacc[r] - dl);   // dS from the fp32 P
+      for (int r = 0; r < 16; ++r) dpacc[r] = sacc[r] * dpacc[r];   // dS from the fp32 P
       bf16x8 sf[2];
       pack2(dpacc, sf[0], sf[1]);
       if constexpr (kRow) {
