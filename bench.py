@@ -65,7 +65,7 @@ def stored_traffic(kernel: str, workload: str):
         rec = json.load(f)
     if rec.get("source_sha256") != source_digest(kernel):
         return None, "kernel changed since the counters were taken"
-    return float(rec["hbm_bytes_per_launch"]), path
+    return float(rec["hbm_bytes_per_launch"]), os.path.relpath(path, ROOT)
 
 
 def replicated_inputs(q, k, v, do, P, lengths):

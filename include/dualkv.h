@@ -77,7 +77,7 @@ size_t dualkv_fwd_workspace_bytes(int P, int R, int N, const int32_t* offsets,
                                   int Hq, int Hkv, int d);
 
 /* Workspace dualkv_bwd needs: the two work lists, the per-row pairs
- * {-LSE * log2(e), D = rowsum(dO*O)} [Hq][T] fp32, and either fp32
+ * {-LSE * log2(e), -D}, D = rowsum(dO*O), [Hq][T] fp32, and either fp32
  * accumulators for dK and dV [T][Hkv][d] (atomic mode) or, with
  * deterministic != 0, per-work-item dK/dV partials plus the lists of
  * each key tile's items (dQ is written directly in both modes). 0 if the
