@@ -35,7 +35,10 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2
 PEAK_HBM_GBS = 8000.0
 METRIC = "fwd+bwd useful TFLOP/s and % bf16 MFMA peak at P=8K,R=4K,N=32"
 PROFILES = os.path.join(ROOT, "profiles")
-_FRAG = ["exact_shared_prefix_amd/csrc/common.h", "exact_shared_prefix_amd/csrc/frag.h"]
+# a kernel's code depends on its source, the shared headers and the build's
+# compiler options
+_FRAG = ["exact_shared_prefix_amd/csrc/common.h", "exact_shared_prefix_amd/csrc/frag.h",
+         "exact_shared_prefix_amd/build.py"]
 KERNEL_SOURCES = {
     "dkv_kernel": ["exact_shared_prefix_amd/csrc/bwd.hip"] + _FRAG,
     "dq_kernel": ["exact_shared_prefix_amd/csrc/bwd.hip"] + _FRAG,
