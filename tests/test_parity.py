@@ -188,6 +188,42 @@ def test_deterministic_mode_bitwise_repeat_multi_chunk():
         assert rel(a[key], c[key]) <= 1e-3, key
 
 
+# ------------------------------------------------------ random packings --
+# Seeded random packings (prompt length, number and lengths of responses,
+# empty responses, head counts that are not powers of two, d = 64 / 128,
+# input scales, both reduction modes), each compared element-wise with the
+# replicated oracle. The shapes come from numpy's generator seeded with the
+# case number; they are test parameters, not part of the method.
+_HEADS = [(2, 1), (4, 2), (4, 4), (6, 3), (8, 2), (3, 1), (5, 5), (12, 4)]
+
+
+def _random_case(i):
+    rng = np.random.default_rng(1000 + i)
+    P = int(rng.integers(0, 601))
+    n = int(rng.integers(1, 6))
+    lengths = [int(x) for x in rng.integers(0, 257, size=n)]
+    if P + sum(lengths) == 0:
+        lengths[0] = 1
+    Hq, Hkv = _HEADS[int(rng.integers(0, len(_HEADS)))]
+    d = (64, 128)[int(rng.integers(0, 2))]
+    qkv_scale = float((0.5, 1.0, 2.0)[int(rng.integers(0, 3))])
+    return dict(P=P, lengths=lengths, Hq=Hq, Hkv=Hkv, d=d, qkv_scale=qkv_scale, seed=2000 + i,
+                det=bool(i % 2))
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_packings_elementwise(i):
+    kw = _random_case(i)
+    det = kw.pop("det")
+    P, lengths, Hq, Hkv, d, seed = (kw.pop(x) for x in ("P", "lengths", "Hq", "Hkv", "d", "seed"))
+    inp = make_inputs(P, lengths, Hq, Hkv, d, seed=seed, **kw)
+    say(f"case random {i}: P={P} lengths={lengths} Hq={Hq} Hkv={Hkv} d={d} qkv_scale={inp.meta['qkv_scale']} "
+        f"deterministic={det}")
+    got = run_gpu(inp, deterministic=det)
+    ref = oracle_fwd_bwd(np64(inp.q), np64(inp.k), np64(inp.v), np64(inp.do), P, lengths, inp.scale)
+    check_all(got, ref, P, f"random {i}")
+
+
 # ------------------------------------------------ across the row-chunk grid --
 # The dK/dV pass cuts every key tile's attending rows into row chunks (2048
 # rows; 256 to 1024 for problems too small to fill the chip with 2048-row
