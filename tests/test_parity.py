@@ -359,6 +359,39 @@ def test_groups_elementwise(name, det):
         assert np.all(np.isfinite(x)), key
 
 
+def _random_groups(i):
+    rng = np.random.default_rng(3000 + i)
+    groups = []
+    for _ in range(int(rng.integers(1, 5))):
+        P = int(rng.integers(0, 300))
+        groups.append((P, [int(x) for x in rng.integers(0, 200, size=int(rng.integers(1, 5)))]))
+    if group_starts(groups)[-1] == 0:
+        groups[0] = (1, groups[0][1])
+    Hq, Hkv = _HEADS[int(rng.integers(0, len(_HEADS)))]
+    d = (64, 128)[int(rng.integers(0, 2))]
+    return groups, Hq, Hkv, d
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_random_groups_elementwise(i):
+    """Seeded random multi-group calls (group counts, prompt and response
+    lengths including empty ones, head layouts, d), alternating modes."""
+    groups, Hq, Hkv, d = _random_groups(i)
+    det = bool(i % 2)
+    T = group_starts(groups)[-1]
+    inp = make_inputs(0, [T], Hq, Hkv, d, seed=3100 + i)
+    say(f"case random groups {i}: {groups} Hq={Hq} Hkv={Hkv} d={d} det={det}")
+    got = run_gpu_groups(inp, groups, det)
+    ref = oracle_groups_fwd_bwd(np64(inp.q), np64(inp.k), np64(inp.v), np64(inp.do), groups, inp.scale)
+    for key in ("O", "dQ", "dK", "dV"):
+        err = rel(got[key], ref[key])
+        say(f"  {key}: rel {err:.2e}")
+        assert err <= REL, key
+    assert float(np.max(np.abs(got["LSE"] - ref["LSE"]))) <= LSE_ABS
+    for key, x in got.items():
+        assert np.all(np.isfinite(x)), key
+
+
 def test_one_group_call_is_the_single_group_call():
     """B = 1 through the group entry points gives the single-group entry
     points' bits (deterministic backward, so dK, dV are ordered too)."""
@@ -402,6 +435,44 @@ def test_tree_elementwise(name):
     got = run_gpu_tree(inp, c["node_len"], c["node_parent"])
     ref = oracle_tree_fwd_bwd(np64(inp.q), np64(inp.k), np64(inp.v), np64(inp.do), c["node_len"],
                               c["node_parent"], inp.scale)
+    for key in ("O", "dQ", "dK", "dV"):
+        e = rel(got[key], ref[key])
+        say(f"  {key}: rel {e:.2e}")
+        assert e <= REL, key
+    assert float(np.max(np.abs(got["LSE"] - ref["LSE"]))) <= LSE_ABS
+    for key, x in got.items():
+        assert np.all(np.isfinite(x)), key
+
+
+def _random_forest(i):
+    """A random prefix forest in depth-first order, at most four levels: each
+    new segment hangs below a segment on the current root-to-leaf path (or
+    starts a new tree)."""
+    rng = np.random.default_rng(4000 + i)
+    node_len, node_parent, depth, path = [], [], [], []
+    for n in range(int(rng.integers(2, 10))):
+        choices = [-1] + [x for x in path if depth[x] < 4]
+        par = choices[int(rng.integers(0, len(choices)))] if n else -1
+        node_len.append(int(rng.integers(0, 160)) if rng.random() > 0.1 else 0)
+        node_parent.append(par)
+        depth.append(1 if par < 0 else depth[par] + 1)
+        path = ([] if par < 0 else path[:path.index(par) + 1]) + [n]
+    if sum(node_len) == 0:
+        node_len[0] = 1
+    Hq, Hkv = _HEADS[int(rng.integers(0, len(_HEADS)))]
+    d = (64, 128)[int(rng.integers(0, 2))]
+    return node_len, node_parent, Hq, Hkv, d
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_random_trees_elementwise(i):
+    node_len, node_parent, Hq, Hkv, d = _random_forest(i)
+    T = sum(node_len)
+    inp = make_inputs(0, [T], Hq, Hkv, d, seed=4100 + i)
+    say(f"case random tree {i}: {node_len} {node_parent} Hq={Hq} Hkv={Hkv} d={d}")
+    got = run_gpu_tree(inp, node_len, node_parent, deterministic=bool(i % 2))
+    ref = oracle_tree_fwd_bwd(np64(inp.q), np64(inp.k), np64(inp.v), np64(inp.do), node_len, node_parent,
+                              inp.scale)
     for key in ("O", "dQ", "dK", "dV"):
         e = rel(got[key], ref[key])
         say(f"  {key}: rel {e:.2e}")
