@@ -159,6 +159,47 @@ def test_repeat_calls_agree_within_tolerance():
         assert rel(a[key], b[key]) <= 1e-3, key
 
 
+def test_backward_phase_by_phase_is_the_whole_backward():
+    """The four backward phases run one call at a time on one workspace
+    (preprocess; dQ before dK/dV, which are independent; finish) give the
+    whole backward's bits (deterministic mode, so dK, dV are ordered)."""
+    inp = make_inputs(300, [129, 1, 0, 64, 250], 4, 2, 128, seed=61)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.do))
+    pk = binding.Packing(inp.P, inp.lengths)
+    o, lse = binding.fwd(q, k, v, pk, inp.scale)
+    whole = binding.bwd(q, k, v, o, lse, do, pk, inp.scale, deterministic=True)
+    ws = torch.empty(binding.bwd_workspace_bytes(pk, 4, 2, 128, True), dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    for ph in (binding.PHASE_PRE, binding.PHASE_DQ, binding.PHASE_MAIN, binding.PHASE_FINISH):
+        binding.bwd(q, k, v, o, lse, do, pk, inp.scale, dq, dk, dv, workspace=ws, deterministic=True,
+                    phases=ph)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dQ", "dK", "dV"), whole, (dq, dk, dv)):
+        assert torch.equal(a, b), name
+
+
+def test_calls_on_a_side_stream_match_the_current_stream():
+    """Forward and backward enqueued on another stream (default priority),
+    outputs and workspaces allocated by the binding for that stream, give the
+    current stream's bits (deterministic backward)."""
+    inp = make_inputs(256, [300, 180, 7], 4, 2, 128, seed=62)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.do))
+    pk = binding.Packing(inp.P, inp.lengths)
+    o, lse = binding.fwd(q, k, v, pk, inp.scale)
+    ref = binding.bwd(q, k, v, o, lse, do, pk, inp.scale, deterministic=True)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    o2, lse2 = binding.fwd(q, k, v, pk, inp.scale, stream=side)
+    got = binding.bwd(q, k, v, o2, lse2, do, pk, inp.scale, deterministic=True, stream=side)
+    side.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    for name, a, b in zip(("dQ", "dK", "dV"), ref, got):
+        assert torch.equal(a, b), name
+
+
 @pytest.mark.parametrize("name", ["ragged_tails_p300", "ragged_d64_many", "gqa8_p192"])
 def test_deterministic_mode_parity_and_bitwise_repeat(name):
     """Deterministic mode: same bar against the oracle, and two calls give
