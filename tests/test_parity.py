@@ -200,6 +200,36 @@ def test_calls_on_a_side_stream_match_the_current_stream():
         assert torch.equal(a, b), name
 
 
+def test_noalloc_forward_replays_in_a_captured_graph():
+    """The allocation-free forward launches only kernels (its work lists are
+    built on the device), so it can be captured in a HIP graph: every replay,
+    with eager work of the same library between them, gives the eager result."""
+    inp = make_inputs(700, [300, 0, 129, 64], 8, 2, 128, seed=63)
+    dev = torch.device("cuda:0")
+    q, k, v = (x.to(dev) for x in (inp.q, inp.k, inp.v))
+    pk = binding.Packing(inp.P, inp.lengths)
+    ref_o, ref_lse = binding.fwd(q, k, v, pk, inp.scale)
+    o = torch.empty_like(ref_o)
+    lse = torch.empty_like(ref_lse)
+    binding.fwd_noalloc(q, k, v, pk, inp.scale, out=o, lse=lse)   # first call: scratch address taken
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        binding.fwd_noalloc(q, k, v, pk, inp.scale, out=o, lse=lse)
+    other = make_inputs(300, [100, 50], 8, 2, 128, seed=64)
+    oq, ok, ov = (x.to(dev) for x in (other.q, other.k, other.v))
+    opk = binding.Packing(other.P, other.lengths)
+    for r in range(3):
+        o.zero_()
+        lse.zero_()
+        binding.fwd_noalloc(oq, ok, ov, opk, other.scale)   # eager, same scratch array
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        say(f"  replay {r}")
+        assert torch.equal(o, ref_o) and torch.equal(lse, ref_lse), r
+
+
 @pytest.mark.parametrize("name", ["ragged_tails_p300", "ragged_d64_many", "gqa8_p192"])
 def test_deterministic_mode_parity_and_bitwise_repeat(name):
     """Deterministic mode: same bar against the oracle, and two calls give
